@@ -1,0 +1,234 @@
+/*
+ * fa_oracle.c -- plain fp64 CPU attention: TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the correctness oracle for the GPU attention library. It is
+ * called only from the test suite, from the smoke check and from the CPU
+ * baseline leg of the benchmark; the product path never links or calls it.
+ * It shares no code, header, table or helper with the GPU kernels.
+ *
+ * What it computes is the plain definition of exact scaled-dot-product
+ * attention, written out with no tiling and no online softmax:
+ *   - "FlashAttention" explainer page, section "What it is": scores = Q K^T,
+ *     softmax of the scores, weights times V (the three standard steps).
+ *   - same page, "Checking correctness": the plain reference computes
+ *     scale * Q K^T with scale = d^-1/2 by default, masks future keys for
+ *     causal attention, then softmax and the product with V.
+ *   - same page, "Step 5": the per-row statistic kept beside O is the log of
+ *     the softmax normaliser (LSE).
+ *   - same page, glossary: causal attention sees itself and earlier
+ *     positions; grouped-query attention shares one K/V head between several
+ *     query heads.
+ *   - "Flash Attention" skill page, "Workflow 2": window_size=(left, right),
+ *     (-1, -1) meaning no window, combinable with causal.
+ *   - "The One-Line Change ... Flash Attention 2 in HuggingFace": packed
+ *     sequences with cumulative lengths never attend across borders.
+ *
+ * Readings taken where the pages are silent (each is also listed in the
+ * design notes of the repository):
+ *   - query head h uses K/V head floor(h / (Hq / Hkv));
+ *   - when Sq != Sk, query row i sits at key position i + (Sk - Sq)
+ *     ("bottom-right" alignment), so a one-token decode query sees its whole
+ *     cache;
+ *   - window bounds are inclusive: pos - left <= j <= pos + right, a negative
+ *     bound means unbounded on that side;
+ *   - LSE is the natural log of sum_j exp(s_ij) over visible keys, where
+ *     s_ij = scale * q_i . k_j;
+ *   - a row with no visible key has O = 0 and LSE = -inf.
+ *
+ * Arithmetic: every step in double precision, two passes per row (max, then
+ * exp/sum/weighted sum).  The only parallelism is OpenMP over independent
+ * rows, which does not change any row's arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Is key j visible from query row i?  Sequence lengths sq (queries) and sk
+ * (keys); causal / window flags as described above. */
+static int visible(long i, long j, long sq, long sk, int causal, int wl, int wr)
+{
+    long pos = i + (sk - sq); /* key-axis position of query row i */
+    if (j < 0 || j >= sk) return 0;
+    if (causal && j > pos) return 0;
+    if (wl >= 0 && j < pos - wl) return 0;
+    if (wr >= 0 && j > pos + wr) return 0;
+    return 1;
+}
+
+static double dot(const double* a, const double* b, int d)
+{
+    double s = 0.0;
+    for (int t = 0; t < d; ++t) s += a[t] * b[t];
+    return s;
+}
+
+/* One query row against one key/value head: scores, max, exp, sum, output.
+ * scores: caller scratch of length sk. */
+static void attend_row(const double* qrow, const double* k, const double* v,
+                       long kv_stride, long i, long sq, long sk, int d,
+                       int causal, int wl, int wr, double scale,
+                       double* orow, double* lse, double* scores)
+{
+    double m = -INFINITY;
+    for (long j = 0; j < sk; ++j) {
+        if (!visible(i, j, sq, sk, causal, wl, wr)) continue;
+        scores[j] = scale * dot(qrow, k + j * kv_stride, d);
+        if (scores[j] > m) m = scores[j];
+    }
+    for (int t = 0; t < d; ++t) orow[t] = 0.0;
+    if (m == -INFINITY) { /* no visible key */
+        *lse = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (long j = 0; j < sk; ++j)
+        if (visible(i, j, sq, sk, causal, wl, wr)) l += exp(scores[j] - m);
+    for (long j = 0; j < sk; ++j) {
+        if (!visible(i, j, sq, sk, causal, wl, wr)) continue;
+        double p = exp(scores[j] - m) / l;
+        const double* vrow = v + j * kv_stride;
+        for (int t = 0; t < d; ++t) orow[t] += p * vrow[t];
+    }
+    *lse = m + log(l);
+}
+
+/* Rows of one (sequence, query head) pair.
+ *   q:   n query rows, row r at q + r*q_stride, with query index qi[r] in a
+ *        sequence of sq queries;
+ *   k,v: sk key/value rows of the matching K/V head, row j at k + j*kv_stride;
+ *   out: n rows at out + r*o_stride; lse: n values.
+ * Returns 0, or -1 if scratch memory could not be allocated. */
+int fa_oracle_rows(const double* q, long q_stride, const int64_t* qi, int n, long sq,
+                   const double* k, const double* v, long kv_stride, long sk, int d,
+                   int causal, int wl, int wr, double scale,
+                   double* out, long o_stride, double* lse)
+{
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scores = (double*)malloc(sizeof(double) * (size_t)(sk > 0 ? sk : 1));
+        if (!scores) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int r = 0; r < n; ++r)
+                attend_row(q + r * q_stride, k, v, kv_stride, qi[r], sq, sk, d,
+                           causal, wl, wr, scale, out + r * o_stride, lse + r, scores);
+            free(scores);
+        }
+    }
+    return err;
+}
+
+/* Padded batch. q,out: [B,Sq,Hq,d]; k,v: [B,Sk,Hkv,d]; lse: [B,Hq,Sq]. */
+int fa_oracle_fwd(const double* q, const double* k, const double* v, double* out, double* lse,
+                  int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                  int causal, int wl, int wr, double scale)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return -2;
+    int G = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scores = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        if (!scores) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+#pragma omp for collapse(3) schedule(dynamic, 16)
+            for (int b = 0; b < B; ++b)
+                for (int h = 0; h < Hq; ++h)
+                    for (int i = 0; i < Sq; ++i) {
+                        int g = h / G;
+                        const double* qrow = q + (((long)b * Sq + i) * Hq + h) * d;
+                        const double* kb = k + ((long)b * Sk * Hkv + g) * d;
+                        const double* vb = v + ((long)b * Sk * Hkv + g) * d;
+                        double* orow = out + (((long)b * Sq + i) * Hq + h) * d;
+                        double* l = lse + ((long)b * Hq + h) * Sq + i;
+                        attend_row(qrow, kb, vb, (long)Hkv * d, i, Sq, Sk, d,
+                                   causal, wl, wr, scale, orow, l, scores);
+                    }
+            free(scores);
+        }
+    }
+    return err;
+}
+
+/* Packed sequences. q,out: [total_q,Hq,d]; k,v: [total_k,Hkv,d];
+ * lse: [Hq,total_q]; sequence z owns query rows [cu_q[z], cu_q[z+1]) and
+ * key rows [cu_k[z], cu_k[z+1]). */
+int fa_oracle_varlen(const double* q, const double* k, const double* v, double* out, double* lse,
+                     const int32_t* cu_q, const int32_t* cu_k, int nseq,
+                     int Hq, int Hkv, int d, int causal, int wl, int wr, double scale)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return -2;
+    int G = Hq / Hkv;
+    long total_q = cu_q[nseq];
+    long max_sk = 1;
+    for (int z = 0; z < nseq; ++z)
+        if (cu_k[z + 1] - cu_k[z] > max_sk) max_sk = cu_k[z + 1] - cu_k[z];
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scores = (double*)malloc(sizeof(double) * (size_t)max_sk);
+        if (!scores) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic, 16)
+            for (long t = 0; t < total_q; ++t)
+                for (int h = 0; h < Hq; ++h) {
+                    int z = 0;
+                    while (!(cu_q[z] <= t && t < cu_q[z + 1])) ++z;
+                    long sq = cu_q[z + 1] - cu_q[z];
+                    long sk = cu_k[z + 1] - cu_k[z];
+                    long i = t - cu_q[z];
+                    int g = h / G;
+                    const double* kb = k + ((long)cu_k[z] * Hkv + g) * d;
+                    const double* vb = v + ((long)cu_k[z] * Hkv + g) * d;
+                    attend_row(q + (t * Hq + h) * d, kb, vb, (long)Hkv * d, i, sq, sk, d,
+                               causal, wl, wr, scale, out + (t * Hq + h) * d,
+                               lse + (long)h * total_q + t, scores);
+                }
+            free(scores);
+        }
+    }
+    return err;
+}
+
+/* One-token decode against a KV cache. q,out: [B,1,Hq,d];
+ * kc,vc: [B,Sk_cap,Hkv,d]; the first cache_seqlens[b] rows of sequence b are
+ * its keys (they include the current token); lse: [B,Hq]. */
+int fa_oracle_decode(const double* q, const double* kc, const double* vc,
+                     const int32_t* cache_seqlens, double* out, double* lse,
+                     int B, int Hq, int Hkv, int Sk_cap, int d,
+                     int causal, int wl, int wr, double scale)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return -2;
+    int G = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scores = (double*)malloc(sizeof(double) * (size_t)(Sk_cap > 0 ? Sk_cap : 1));
+        if (!scores) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic, 1)
+            for (int b = 0; b < B; ++b)
+                for (int h = 0; h < Hq; ++h) {
+                    long sk = cache_seqlens[b];
+                    int g = h / G;
+                    const double* kb = kc + ((long)b * Sk_cap * Hkv + g) * d;
+                    const double* vb = vc + ((long)b * Sk_cap * Hkv + g) * d;
+                    attend_row(q + ((long)b * Hq + h) * d, kb, vb, (long)Hkv * d, 0, 1, sk, d,
+                               causal, wl, wr, scale, out + ((long)b * Hq + h) * d,
+                               lse + (long)b * Hq + h, scores);
+                }
+            free(scores);
+        }
+    }
+    return err;
+}

@@ -1,0 +1,211 @@
+"""fp64 CPU attention oracle: TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+import this module.  The GPU library never imports, links or calls it, and
+this module imports nothing from the GPU package.
+
+The arithmetic lives in ``fa_oracle.c`` (plain double-precision definition of
+attention; see the header of that file for the passages it follows and the
+readings taken where the pages are silent).  This module only builds that
+file with gcc, converts inputs exactly to float64 and marshals arguments.
+
+Every input is converted with an exact widening cast (bf16/fp16/fp32 to
+fp64), so the oracle sees precisely the values the GPU sees.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "fa_oracle.c")
+LIB = os.path.join(_HERE, "libfa_oracle.so")
+
+_lock = threading.Lock()
+_lib_cache: dict[str, ctypes.CDLL] = {}
+
+
+def build(src: str = SRC, out: str = LIB, extra_flags: tuple[str, ...] = ()) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP over rows)."""
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+           *extra_flags, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return out
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_long, ctypes.c_double
+    lib.fa_oracle_rows.argtypes = [P, i64, P, i32, i64, P, P, i64, i64, i32,
+                                   i32, i32, i32, f64, P, i64, P]
+    lib.fa_oracle_fwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                  i32, i32, i32, f64]
+    lib.fa_oracle_varlen.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32,
+                                     i32, i32, i32, f64]
+    lib.fa_oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                     i32, i32, i32, f64]
+    for f in (lib.fa_oracle_rows, lib.fa_oracle_fwd, lib.fa_oracle_varlen,
+              lib.fa_oracle_decode):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def load(path: str = LIB) -> ctypes.CDLL:
+    """Load (building first if the shared object is missing) the oracle."""
+    with _lock:
+        if path in _lib_cache:
+            return _lib_cache[path]
+        if not os.path.exists(path):
+            if path != LIB:
+                raise FileNotFoundError(path)
+            build()
+        lib = _bind(ctypes.CDLL(path))
+        _lib_cache[path] = lib
+        return lib
+
+
+def _f64(x) -> np.ndarray:
+    """Exact widening to a contiguous float64 numpy array."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float64).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _i32(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu").numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _scale(scale, d: int) -> float:
+    # Default scale 1/sqrt(d): "Checking correctness" on the FlashAttention
+    # explainer page; softmax_scale=None on the skill page.
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+class Oracle:
+    """Thin marshalling wrapper around one loaded oracle shared object."""
+
+    def __init__(self, lib: ctypes.CDLL | None = None):
+        self.lib = lib if lib is not None else load()
+
+    # -- padded batch ------------------------------------------------------
+    def attention(self, q, k, v, causal=False, window=(-1, -1), scale=None):
+        """q: [B,Sq,Hq,d]; k,v: [B,Sk,Hkv,d] -> (out [B,Sq,Hq,d], lse [B,Hq,Sq])."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, Sq, Hq, d = q.shape
+        Bk, Sk, Hkv, dk = k.shape
+        assert Bk == B and dk == d and v.shape == k.shape
+        out = np.empty_like(q)
+        lse = np.empty((B, Hq, Sq), dtype=np.float64)
+        rc = self.lib.fa_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                    B, Hq, Hkv, Sq, Sk, d, int(bool(causal)),
+                                    int(window[0]), int(window[1]), _scale(scale, d))
+        if rc != 0:
+            raise RuntimeError(f"oracle fwd failed: {rc}")
+        return out, lse
+
+    # -- packed sequences --------------------------------------------------
+    def attention_varlen(self, q, k, v, cu_q, cu_k, causal=False, window=(-1, -1),
+                         scale=None):
+        """q: [total_q,Hq,d]; k,v: [total_k,Hkv,d]; cu_*: [nseq+1]
+        -> (out [total_q,Hq,d], lse [Hq,total_q])."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        cu_q, cu_k = _i32(cu_q), _i32(cu_k)
+        total_q, Hq, d = q.shape
+        _, Hkv, _ = k.shape
+        nseq = cu_q.shape[0] - 1
+        assert cu_k.shape[0] == nseq + 1 and cu_q[-1] == total_q
+        assert cu_k[-1] <= k.shape[0]
+        out = np.empty_like(q)
+        lse = np.empty((Hq, total_q), dtype=np.float64)
+        rc = self.lib.fa_oracle_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                       _ptr(cu_q), _ptr(cu_k), nseq, Hq, Hkv, d,
+                                       int(bool(causal)), int(window[0]), int(window[1]),
+                                       _scale(scale, d))
+        if rc != 0:
+            raise RuntimeError(f"oracle varlen failed: {rc}")
+        return out, lse
+
+    # -- decode --------------------------------------------------------------
+    def attention_decode(self, q, k_cache, v_cache, cache_seqlens, causal=False,
+                         window=(-1, -1), scale=None):
+        """q: [B,1,Hq,d]; caches: [B,Sk_cap,Hkv,d]; cache_seqlens: [B]
+        -> (out [B,1,Hq,d], lse [B,Hq])."""
+        q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+        sl = _i32(cache_seqlens)
+        B, one, Hq, d = q.shape
+        assert one == 1
+        _, Sk_cap, Hkv, _ = kc.shape
+        assert (sl >= 0).all() and (sl <= Sk_cap).all()
+        out = np.empty_like(q)
+        lse = np.empty((B, Hq), dtype=np.float64)
+        rc = self.lib.fa_oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(sl), _ptr(out),
+                                       _ptr(lse), B, Hq, Hkv, Sk_cap, d, int(bool(causal)),
+                                       int(window[0]), int(window[1]), _scale(scale, d))
+        if rc != 0:
+            raise RuntimeError(f"oracle decode failed: {rc}")
+        return out, lse
+
+    # -- sampled rows of one (sequence, head) ------------------------------
+    def attention_rows(self, q_rows, qi, sq, k_seq, v_seq, causal=False,
+                       window=(-1, -1), scale=None):
+        """q_rows: [n,d] query rows with indices qi[n] in a sequence of sq
+        queries; k_seq, v_seq: [sk,d] of the matching K/V head.
+        -> (out [n,d], lse [n])."""
+        q, k, v = _f64(q_rows), _f64(k_seq), _f64(v_seq)
+        qi = np.ascontiguousarray(np.asarray(qi, dtype=np.int64))
+        n, d = q.shape
+        sk = k.shape[0]
+        out = np.empty((n, d), dtype=np.float64)
+        lse = np.empty((n,), dtype=np.float64)
+        rc = self.lib.fa_oracle_rows(_ptr(q), d, _ptr(qi), n, int(sq), _ptr(k), _ptr(v), d,
+                                     sk, d, int(bool(causal)), int(window[0]),
+                                     int(window[1]), _scale(scale, d), _ptr(out), d,
+                                     _ptr(lse))
+        if rc != 0:
+            raise RuntimeError(f"oracle rows failed: {rc}")
+        return out, lse
+
+
+_default: Oracle | None = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def attention(*a, **kw):
+    return default().attention(*a, **kw)
+
+
+def attention_varlen(*a, **kw):
+    return default().attention_varlen(*a, **kw)
+
+
+def attention_decode(*a, **kw):
+    return default().attention_decode(*a, **kw)
+
+
+def attention_rows(*a, **kw):
+    return default().attention_rows(*a, **kw)

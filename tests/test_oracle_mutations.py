@@ -1,0 +1,63 @@
+"""Plausible mistakes planted in a copy of the oracle (on the CPU) must each
+fail at least one pin: evidence that the pins constrain every part of the
+oracle (mask predicate, alignment, GQA mapping, scale, normaliser, LSE,
+operand choice, layouts, packed and decode indexing)."""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import PINS
+
+MUTANTS = {
+    "top_left_alignment": ("long pos = i + (sk - sq);", "long pos = i;"),
+    "causal_off_by_one": ("if (causal && j > pos) return 0;", "if (causal && j >= pos) return 0;"),
+    "window_left_exclusive": ("if (wl >= 0 && j < pos - wl) return 0;",
+                              "if (wl >= 0 && j <= pos - wl) return 0;"),
+    "window_right_ignored_at_zero": ("if (wr >= 0 && j > pos + wr) return 0;",
+                                     "if (wr > 0 && j > pos + wr) return 0;"),
+    "window_sides_swapped": ("if (wl >= 0 && j < pos - wl) return 0;",
+                             "if (wr >= 0 && j < pos - wr) return 0;"),
+    "dropped_scale": ("scores[j] = scale * dot(qrow, k + j * kv_stride, d);",
+                      "scores[j] = dot(qrow, k + j * kv_stride, d);"),
+    "lse_without_max": ("*lse = m + log(l);", "*lse = log(l);"),
+    "unnormalised_weights": ("double p = exp(scores[j] - m) / l;",
+                             "double p = exp(scores[j] - m);"),
+    "sum_without_max_shift": ("l += exp(scores[j] - m);", "l += exp(scores[j]);"),
+    "keys_used_as_values": ("const double* vrow = v + j * kv_stride;",
+                            "const double* vrow = k + j * kv_stride;"),
+    "gqa_modulo_mapping": ("int g = h / G;\n                        const double* qrow",
+                           "int g = h % Hkv;\n                        const double* qrow"),
+    "kv_head_ignored": ("const double* kb = k + ((long)b * Sk * Hkv + g) * d;",
+                        "const double* kb = k + ((long)b * Sk * Hkv) * d;"),
+    "q_layout_bhsd": ("const double* qrow = q + (((long)b * Sq + i) * Hq + h) * d;",
+                      "const double* qrow = q + (((long)b * Hq + h) * Sq + i) * d;"),
+    "lse_layout_bsh": ("double* l = lse + ((long)b * Hq + h) * Sq + i;",
+                       "double* l = lse + ((long)b * Sq + i) * Hq + h;"),
+    "varlen_global_row_index": ("long i = t - cu_q[z];", "long i = t;"),
+    "varlen_key_offset_from_q": ("const double* kb = k + ((long)cu_k[z] * Hkv + g) * d;",
+                                 "const double* kb = k + ((long)cu_q[z] * Hkv + g) * d;"),
+    "decode_reads_whole_cache": ("long sk = cache_seqlens[b];", "long sk = Sk_cap;"),
+    "decode_gqa_modulo": ("int g = h / G;\n                    const double* kb = kc",
+                          "int g = h % Hkv;\n                    const double* kb = kc"),
+    "max_not_tracked": ("if (scores[j] > m) m = scores[j];", "if (m == -INFINITY) m = scores[j];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site not unique: {name}"
+    mut_src = tmp_path / "fa_oracle_mut.c"
+    mut_src.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "libfa_oracle_mut.so")
+    oracle.build(str(mut_src), lib_path)
+    orc = oracle.Oracle(oracle.load(lib_path))
+    failed = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except (AssertionError, RuntimeError, FloatingPointError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
