@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+A step is one call of the hot path on the headline workload: causal GQA
+prefill, B=4, Hq=32, Hkv=8, S=4096, d=128, bf16 (one fa_fwd launch).  The
+KV-cache decode workload (B=64, Hq=32, Hkv=8, d=128, cache lengths
+U{1024..32768}, split 1024 + combine) is timed beside it and reported under
+"decode".  Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line (rank 0).  --gpus N with N > 1 is refused: this build
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from exact_attention_08_amd import fa, metrics, synth  # noqa: E402
+
+METRIC = "attn fwd TFLOP/s (causal-adj) & % bf16 MFMA peak; decode HBM GB/s"
+
+
+def _timed(fn, steps: int, warmup: int):
+    """W untimed calls, then exactly K timed calls bracketed by synchronize;
+    returns (wall ms per step, event ms per step on the launch stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, e0.elapsed_time(e1) / steps
+
+
+def bench_prefill(steps, warmup, w):
+    q, k, v = synth.generate(w)
+    dev = "cuda:0"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    work = metrics.fwd_work(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window)
+
+    def step():
+        fa.fwd(qd, kd, vd, causal=w.causal, window=w.window, out=out, lse=lse)
+
+    wall, ev = _timed(step, steps, warmup)
+    return q, k, v, work, wall, ev
+
+
+def bench_decode(steps, warmup):
+    w = synth.WORKLOADS["kvcache_decode"]
+    q, kc, vc, sl = synth.generate(w)
+    dev = "cuda:0"
+    qd, kd, vd, sld = q.to(dev), kc.to(dev), vc.to(dev), sl.to(dev)
+    del kc, vc
+    mx = int(sl.max())
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.Hq, mx, w.d, w.split), dtype=torch.uint8,
+                     device=dev)
+    work = metrics.decode_work(sl.tolist(), w.Hq, w.Hkv, w.d)
+
+    def step():
+        fa.decode_kvcache(qd, kd, vd, sld, mx, split_size=w.split, out=out, lse=lse, workspace=ws)
+
+    wall, ev = _timed(step, steps, warmup)
+    gbs = work["bytes"] / (ev * 1e-3) / 1e9
+    res = {"workload": w.name, "value": round(gbs, 1), "unit": "GB/s",
+           "ms_per_step": round(wall, 4), "event_ms_per_call": round(ev, 4),
+           "frac_hbm_peak": round(gbs / metrics.PEAK_HBM_GBS, 4),
+           "algorithmic_bytes": work["bytes"], "kernels_per_call": 2,
+           "cache_lengths": {"min": int(sl.min()), "max": mx, "sum": int(sl.sum())}}
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(q, k, v, w, budget_s: float):
+    """The fp64 oracle on the host cores over whole (sequence, head) slices
+    of the same workload, as many as fit in about budget_s seconds."""
+    import oracle
+    orc = oracle.Oracle()
+    G = w.Hq // w.Hkv
+    n_done, flop, t_total = 0, 0, 0.0
+    rows = list(range(w.Sq))
+    for b in range(w.B):
+        for h in range(w.Hq):
+            t0 = time.perf_counter()
+            orc.attention_rows(q[b, :, h], rows, w.Sq, k[b, :, h // G], v[b, :, h // G],
+                               causal=w.causal, window=w.window, scale=w.scale)
+            t_total += time.perf_counter() - t0
+            n_done += 1
+            flop += 4 * w.d * metrics.visible_pairs(w.Sq, w.Sk, w.causal, w.window)
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_done} of {w.B * w.Hq} (sequence, head) slices of {w.name}, all "
+                      f"{w.Sq} rows each, fp64, {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="causal_gqa_prefill",
+                    choices=[n for n, w in synth.WORKLOADS.items() if w.kind == "fwd"])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this attention build runs on exactly one GPU; --gpus must be 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load()   # fails loudly if the HIP library is not built
+
+    w = synth.WORKLOADS[args.workload]
+    q, k, v, work, wall, ev = bench_prefill(args.steps, args.warmup, w)
+    tflops_wall = work["flop"] / (wall * 1e-3) / 1e12
+    tflops_ev = work["flop"] / (ev * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tflops_wall, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq,
+                   "Sk": w.Sk, "d": w.d, "causal": w.causal, "window": list(w.window),
+                   "algorithmic_flop": work["flop"], "algorithmic_bytes": work["bytes"],
+                   "frac_bf16_mfma_peak": round(tflops_wall / metrics.PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel<128,bf16>",
+                     "achieved": round(tflops_ev, 2), "peak": metrics.PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_ev / metrics.PEAK_BF16_TFLOPS, 4),
+                     "avg_launch_ms": round(ev, 5), "traffic": None},
+    }
+    if not args.no_decode:
+        del q
+        line["decode"] = bench_decode(max(10, args.steps // 2), max(3, args.warmup // 2))
+        q = None
+    if args.cpu_budget > 0:
+        if q is None:
+            q, k, v = synth.generate(w)
+        line["cpu_baseline"] = cpu_baseline(q, k, v, w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: host-side argument
+// validation, kernel-parameter setup and launch on the caller's stream.
+// Every argument check runs before any HIP call, so an invalid call touches
+// neither the device nor the runtime.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "fa_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status_t fail(fa_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fa_status_t ok() {
+    g_err[0] = '\0';
+    return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Checks shared by all entry points.
+// k and v may be null only when there are no keys at all (no_keys).
+fa_status_t check_common(const void* q, const void* k, const void* v, const void* out,
+                         const float* lse, int B, int Hq, int Hkv, int d, int wl, int wr,
+                         float scale, fa_dtype_t dtype, bool no_keys = false) {
+    if (!q || !out) return fail(FA_ERR_INVALID_ARG, "q and out must be non-null");
+    if ((!k || !v) && !no_keys)
+        return fail(FA_ERR_INVALID_ARG, "k and v must be non-null when there are keys");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(FA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+    if (lse && !aligned4(lse)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+    if (B < 1 || Hq < 1 || Hkv < 1)
+        return fail(FA_ERR_INVALID_ARG, "B, Hq, Hkv must be >= 1 (got %d, %d, %d)", B, Hq, Hkv);
+    if (Hq % Hkv != 0)
+        return fail(FA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", d);
+    if (dtype != FA_BF16 && dtype != FA_FP16)
+        return fail(FA_ERR_UNSUPPORTED, "dtype %d unsupported (bf16 or fp16)", (int)dtype);
+    if (wl < -1 || wr < -1)
+        return fail(FA_ERR_INVALID_ARG, "window bounds must be >= -1 (got %d, %d)", wl, wr);
+    if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "softmax_scale must be finite");
+    return FA_OK;
+}
+
+void set_scale(float scale, float* c, uint32_t* qsign) {
+    // scores are scaled in fp32 inside the exponent; a negative scale is
+    // folded into an exact sign flip of q so that c >= 0.
+    *c = std::fabs(scale) * fa::kLog2e_host;
+    *qsign = scale < 0.f ? 0x80008000u : 0u;
+}
+
+fa_status_t launch_status(hipError_t e) {
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+constexpr long long kMaxGridThreads = (1ll << 32) - 1;
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                   int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                   int window_right, float softmax_scale, fa_dtype_t dtype, hipStream_t stream) {
+    fa_status_t st = check_common(q, k, v, out, lse, B, Hq, Hkv, d, window_left, window_right,
+                                  softmax_scale, dtype, Sk == 0);
+    if (st != FA_OK) return st;
+    if (Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARG, "Sq, Sk must be >= 0 (got %d, %d)", Sq, Sk);
+    if (Sq == 0) return ok();
+    fa::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+    p.cu_q = nullptr; p.cu_k = nullptr;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sq = Sq; p.Sk = Sk;
+    p.nqt = (Sq + fa::kFwdBM - 1) / fa::kFwdBM;
+    p.q_tok_stride = (long long)Hq * d;
+    p.kv_tok_stride = (long long)Hkv * d;
+    p.lse_b_stride = (long long)Hq * Sq;
+    p.lse_h_stride = Sq;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    set_scale(softmax_scale, &p.c, &p.qsign);
+    p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
+    if ((long long)p.nqt * Hq * B * 256 > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
+}
+
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
+                          int Hkv, int max_seqlen_q, int max_seqlen_k, int total_q, int d,
+                          int causal, int window_left, int window_right, float softmax_scale,
+                          fa_dtype_t dtype, hipStream_t stream) {
+    fa_status_t st = check_common(q, k, v, out, lse, B, Hq, Hkv, d, window_left, window_right,
+                                  softmax_scale, dtype, max_seqlen_k == 0);
+    if (st != FA_OK) return st;
+    if (!cu_seqlens_q || !cu_seqlens_k)
+        return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be non-null");
+    if (!aligned4(cu_seqlens_q) || !aligned4(cu_seqlens_k))
+        return fail(FA_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+    if (max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0)
+        return fail(FA_ERR_INVALID_ARG, "max_seqlen_q, max_seqlen_k, total_q must be >= 0");
+    if (max_seqlen_q == 0 || total_q == 0) return ok();
+    fa::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+    p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sq = max_seqlen_q; p.Sk = max_seqlen_k;
+    p.nqt = (max_seqlen_q + fa::kFwdBM - 1) / fa::kFwdBM;
+    p.q_tok_stride = (long long)Hq * d;
+    p.kv_tok_stride = (long long)Hkv * d;
+    p.lse_b_stride = 0;
+    p.lse_h_stride = total_q;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    set_scale(softmax_scale, &p.c, &p.qsign);
+    p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
+    if ((long long)p.nqt * Hq * B * 256 > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, true, stream));
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int max_seqlen_k, int d, int split_size) {
+    if (B < 1 || Hq < 1 || max_seqlen_k < 1 || d < 1 || split_size < 1) return 0;
+    const size_t nsplit = ((size_t)max_seqlen_k + split_size - 1) / split_size;
+    return (size_t)B * Hq * nsplit * ((size_t)d + 1) * sizeof(float);
+}
+
+fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cache_seqlens, void* out, float* lse, int B, int Hq,
+                              int Hkv, int Sk_cap, int max_seqlen_k, int d, int causal,
+                              int window_left, int window_right, float softmax_scale,
+                              int split_size, void* workspace, size_t workspace_bytes,
+                              fa_dtype_t dtype, hipStream_t stream) {
+    fa_status_t st = check_common(q, k_cache, v_cache, out, lse, B, Hq, Hkv, d, window_left,
+                                  window_right, softmax_scale, dtype);
+    if (st != FA_OK) return st;
+    if (!cache_seqlens || !aligned4(cache_seqlens))
+        return fail(FA_ERR_INVALID_ARG, "cache_seqlens must be non-null and 4-byte aligned");
+    if (Sk_cap < 1) return fail(FA_ERR_INVALID_ARG, "Sk_cap must be >= 1 (got %d)", Sk_cap);
+    if (max_seqlen_k < 1 || max_seqlen_k > Sk_cap)
+        return fail(FA_ERR_INVALID_ARG, "max_seqlen_k must be in [1, Sk_cap] (got %d)", max_seqlen_k);
+    if (split_size < 64 || split_size % 64 != 0)
+        return fail(FA_ERR_INVALID_ARG, "split_size must be a positive multiple of 64 (got %d)",
+                    split_size);
+    const size_t need = fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d, split_size);
+    if (!workspace || !aligned16(workspace))
+        return fail(FA_ERR_WORKSPACE, "workspace must be non-null and 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    fa::DecodeParams p{};
+    p.q = q; p.k = k_cache; p.v = v_cache; p.o = out; p.lse = lse;
+    p.seqlens = cache_seqlens;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sk_cap = Sk_cap;
+    p.max_len = max_seqlen_k;
+    p.split = split_size;
+    p.nsplit = (max_seqlen_k + split_size - 1) / split_size;
+    p.qblocks = (p.G + 31) / 32;
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = p.ws_o + (size_t)B * Hq * p.nsplit * d;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    set_scale(softmax_scale, &p.c, &p.qsign);
+    if ((long long)p.nsplit * p.qblocks * Hkv * B * 64 > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
+}
+
+const char* fa_status_str(fa_status_t s) {
+    switch (s) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// fa_device.hpp -- gfx950 device helpers shared by the attention kernels:
+// vector types, the 32x32x16 MFMA wrappers, 16-bit packing and wave-level
+// exchanges.  Everything here is CDNA4-only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// One v_mfma_f32_32x32x16_{bf16,f16}: C[32x32] += A[32x16] * B[16x32].
+// Operand registers: lane l holds row (A) / column (B) l%32 and the 8
+// reduction slots of half l/32.  Result: lane l holds column l%32, element
+// 4*jj+k of the accumulator is row 8*jj + 4*(l/32) + k.
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
+// Two fp32 -> one dword of two 16-bit values, round to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950 for bf16).
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if constexpr (BF16) {
+        bf16x2 r = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+        return __builtin_bit_cast(uint32_t, r);
+    } else {
+        f16x2 r = __builtin_convertvector((f32x2){lo, hi}, f16x2);
+        return __builtin_bit_cast(uint32_t, r);
+    }
+}
+
+// Build one dword from the low (SEL_HI=false) or high 16-bit halves of two
+// dwords: result = {half(lo_src), half(hi_src)}.
+template <bool SEL_HI>
+__device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, uint32_t hi_src) {
+    // v_perm_b32: byte selector over {hi_src (bytes 4-7), lo_src (bytes 0-3)}
+    return __builtin_amdgcn_perm(hi_src, lo_src, SEL_HI ? 0x07060302u : 0x05040100u);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value held by lane l ^ 32 (the other half of a 64-wide wave).
+__device__ __forceinline__ float xor32(float x) {
+    return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ bool wave_any(bool p) {
+    return __builtin_amdgcn_ballot_w64(p) != 0ull;
+}
+
+// 16-byte / 8-byte global and LDS accesses.
+__device__ __forceinline__ u32x4 ld_global16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ld_global8(const void* p) {
+    return *reinterpret_cast<const u32x2*>(p);
+}
+__device__ __forceinline__ void st_global8(void* p, u32x2 v) {
+    *reinterpret_cast<u32x2*>(p) = v;
+}
+
+}  // namespace fa

@@ -1,0 +1,60 @@
+// fa_internal.hpp -- parameter blocks shared by the host launcher (fa_api.cpp)
+// and the kernels (fa_fwd.hip, fa_decode.hip).  Host-side only types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Forward (padded or packed).  Element strides are in 16-bit elements.
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;                 // may be null
+    const int32_t* cu_q;        // packed only
+    const int32_t* cu_k;        // packed only
+    int B, Hq, Hkv, G;          // G = Hq / Hkv
+    int Sq, Sk;                 // padded: lengths; packed: host upper bounds
+    int nqt;                    // query tiles per (sequence, head)
+    long long q_tok_stride;     // elements between consecutive tokens of q/o (Hq*d)
+    long long kv_tok_stride;    // elements between consecutive tokens of k/v (Hkv*d)
+    long long lse_b_stride;     // padded: Hq*Sq; packed: 0
+    long long lse_h_stride;     // padded: Sq; packed: total_q
+    int causal, wl, wr;
+    float c;                    // |scale| * log2(e)
+    uint32_t qsign;             // 0x80008000 when scale < 0 (q negated exactly), else 0
+    int xcd_groups;             // (B*Hkv)/8 when B*Hkv % 8 == 0, else 0 (no remap)
+};
+
+// Decode split kernel + combine kernel.
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;                 // may be null
+    const int32_t* seqlens;
+    float* ws_o;                // [B, Hq, nsplit, d] fp32 partial outputs
+    float* ws_lse;              // [B, Hq, nsplit] fp32 partial LSEs
+    int B, Hq, Hkv, G;
+    int Sk_cap;
+    int max_len;                // host bound on cache lengths (lengths are clamped to it)
+    int nsplit, split;
+    int qblocks;                // ceil(G / 32)
+    int causal, wl, wr;
+    float c;                    // |scale| * log2(e)
+    uint32_t qsign;
+};
+
+// Host launchers (defined next to their kernels).
+hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
+
+// Kernel tile geometry, shared with the host for grid sizing.
+constexpr int kFwdBM = 128;     // query rows per work-group (4 waves x 32)
+constexpr float kLog2e_host = 1.4426950408889634f;
+
+}  // namespace fa

@@ -1,0 +1,175 @@
+"""Python binding of libfa355.so (include/fa.h) over torch tensors.
+
+Argument marshalling only: shape/dtype/device checks, output allocation with
+torch, the current torch stream, and a ctypes call into the C ABI.  Every
+step of the attention itself runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or a call fails, a RuntimeError says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa355.so")
+
+FA_BF16, FA_FP16 = 0, 1
+_DTYPE = {torch.bfloat16: FA_BF16, torch.float16: FA_FP16}
+STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_ERR_WORKSPACE",
+          4: "FA_ERR_HIP"}
+
+# Every symbol include/fa.h declares.
+EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
+           "fa_status_str", "fa_last_error")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-OK status returned by the C ABI."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library and declare its C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: the HIP library is not built "
+                "(run __graft_entry__.build()); there is no fallback path")
+        lib = ctypes.CDLL(path)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
+        lib.fa_fwd.restype = I
+        lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P]
+        lib.fa_fwd_varlen.restype = I
+        lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+        lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_decode_kvcache.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
+                                          ctypes.c_size_t, I, P]
+        lib.fa_decode_kvcache.restype = I
+        lib.fa_status_str.argtypes = [I]
+        lib.fa_status_str.restype = ctypes.c_char_p
+        lib.fa_last_error.argtypes = []
+        lib.fa_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FAError(status, load().fa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _scale(softmax_scale, d: int) -> float:
+    # None -> 1/sqrt(head_dim), as flash_attn_func's softmax_scale=None
+    return 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensors(*ts):
+    dt = ts[0].dtype
+    _require(dt in _DTYPE, f"dtype {dt} unsupported (bf16 or fp16)")
+    for t in ts:
+        _require(t.is_cuda, "tensors must be on a GPU")
+        _require(t.dtype == dt, "q, k, v must share one dtype")
+        _require(t.is_contiguous(), "tensors must be contiguous")
+
+
+def fwd(q, k, v, *, causal=False, window=(-1, -1), softmax_scale=None, out=None, lse=None):
+    """Padded batch: q [B,Sq,Hq,d], k/v [B,Sk,Hkv,d] -> (out [B,Sq,Hq,d], lse [B,Hq,Sq] fp32)."""
+    _check_tensors(q, k, v)
+    _require(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "expected 4-d q, k, v")
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    _require(k.shape[0] == B and k.shape[3] == d, "k/v batch or head_dim mismatch")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                         int(bool(causal)), int(window[0]), int(window[1]),
+                         _scale(softmax_scale, d), _DTYPE[q.dtype], _stream()))
+    return out, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+               window=(-1, -1), softmax_scale=None, out=None, lse=None):
+    """Packed: q [total_q,Hq,d], k/v [total_k,Hkv,d], cu_seqlens int32 [B+1] on the GPU
+    -> (out [total_q,Hq,d], lse [Hq,total_q] fp32)."""
+    _check_tensors(q, k, v)
+    _require(q.dim() == 3 and k.dim() == 3 and k.shape == v.shape, "expected 3-d q, k, v")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        _require(cu.is_cuda and cu.dtype == torch.int32 and cu.dim() == 1 and cu.is_contiguous(),
+                 "cu_seqlens must be contiguous int32 GPU vectors")
+    total_q, Hq, d = q.shape
+    _, Hkv, _ = k.shape
+    B = cu_seqlens_q.numel() - 1
+    _require(B >= 1 and cu_seqlens_k.numel() == B + 1, "cu_seqlens must have B+1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check(load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv,
+                                int(max_seqlen_q), int(max_seqlen_k), total_q, d,
+                                int(bool(causal)), int(window[0]), int(window[1]),
+                                _scale(softmax_scale, d), _DTYPE[q.dtype], _stream()))
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, max_seqlen_k: int, d: int, split_size: int) -> int:
+    return int(load().fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d, split_size))
+
+
+def decode_kvcache(q, k_cache, v_cache, cache_seqlens, max_seqlen_k, *, causal=False,
+                   window=(-1, -1), softmax_scale=None, split_size=1024, out=None, lse=None,
+                   workspace=None):
+    """One-token decode: q [B,1,Hq,d], caches [B,Sk_cap,Hkv,d], cache_seqlens int32 [B]
+    on the GPU -> (out [B,1,Hq,d], lse [B,Hq] fp32).  The fp32 workspace is allocated
+    with torch unless given (uint8 tensor of at least decode_workspace_bytes)."""
+    _check_tensors(q, k_cache, v_cache)
+    _require(q.dim() == 4 and q.shape[1] == 1, "q must be [B,1,Hq,d]")
+    _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "caches must be [B,Sk_cap,Hkv,d]")
+    _require(cache_seqlens.is_cuda and cache_seqlens.dtype == torch.int32,
+             "cache_seqlens must be an int32 GPU vector")
+    B, _, Hq, d = q.shape
+    _, Sk_cap, Hkv, _ = k_cache.shape
+    lib = load()
+    need = int(lib.fa_decode_workspace_bytes(B, Hq, int(max_seqlen_k), d, int(split_size)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.fa_decode_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens),
+                                 _ptr(out), _ptr(lse), B, Hq, Hkv, Sk_cap, int(max_seqlen_k), d,
+                                 int(bool(causal)), int(window[0]), int(window[1]),
+                                 _scale(softmax_scale, d), int(split_size), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(),
+                                 _DTYPE[q.dtype], _stream()))
+    return out, lse

@@ -1,0 +1,148 @@
+/*
+ * fa.h -- C ABI of the fused exact-attention forward library for MI355X
+ * (gfx950).  Link against libfa355.so.
+ *
+ * What is computed (all entry points): exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T + mask) V,   LSE = log of the softmax normaliser,
+ * in one fused, tiled pass with an online (running max / running sum)
+ * softmax, so the score matrix never reaches device memory.
+ *   - "FlashAttention" explainer page, sections "What it is" and "How it
+ *     works", steps 1-5 (tiling, on-chip scores, online softmax, one final
+ *     normalisation, the saved per-row log-normaliser);
+ *   - same page, step 6 (causal masking with whole-tile skipping), step 7
+ *     (work spread over query blocks, heads and batch), step 8 (16-bit
+ *     operands, fp32 accumulation and fp32 softmax statistics), step 9
+ *     (decoding against a cache, split along the sequence and combined);
+ *   - "Flash Attention" skill page, "Workflow 2": the flash_attn_func
+ *     arguments (causal, window_size=(left, right), softmax_scale) and the
+ *     [batch, seq_len, num_heads, head_dim] layout;
+ *   - "The One-Line Change ... Flash Attention 2 in HuggingFace": packed
+ *     sequences described by cumulative lengths, never attending across
+ *     sequence borders.
+ *
+ * Mask semantics shared by every entry point.  For a sequence with sq query
+ * rows and sk keys, query row i sits at key position pos = i + (sk - sq)
+ * (bottom-right alignment; identical to top-left when sq == sk).  Key j is
+ * visible from row i iff 0 <= j < sk and
+ *     (!causal || j <= pos) && (window_left < 0 || j >= pos - window_left)
+ *                           && (window_right < 0 || j <= pos + window_right).
+ * Window bounds are inclusive; -1 means unbounded on that side.  Query head
+ * h reads K/V head h / (Hq / Hkv) (grouped-query attention by consecutive
+ * groups).  LSE is the natural log of sum_j exp(scale * q_i . k_j) over
+ * visible keys; a row with no visible key gets O = 0 and LSE = -inf.
+ *
+ * Conventions for every entry point.
+ *   - Pointers are DEVICE pointers, owned by the caller, 16-byte aligned,
+ *     dense (no strides beyond the layouts stated).  k and v may be NULL
+ *     only when there are no keys (Sk == 0, or max_seqlen_k == 0 packed).  The library never
+ *     allocates or frees device memory, never keeps a pointer after it
+ *     returns and never synchronises: all work is enqueued on `stream`
+ *     (NULL = the null stream) and the call returns before it runs.
+ *   - q/k/v/out are bf16 or fp16 (dtype); lse and workspaces are fp32;
+ *     cumulative lengths and cache lengths are int32.
+ *   - softmax_scale: any finite value (the Python layer maps "None" to
+ *     1/sqrt(d)); it is applied in fp32 to the fp32 score accumulator.
+ *   - Errors: argument problems are detected on the host before anything is
+ *     enqueued and nothing is written (FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED,
+ *     FA_ERR_WORKSPACE); a failed launch returns FA_ERR_HIP.  The detail of
+ *     the last non-OK return of the calling thread is in fa_last_error().
+ *     There is no fallback path.
+ *   - Not checked (that would need a device-to-host copy): monotone
+ *     cumulative lengths starting at 0, cache lengths within [0, max_seqlen_k].
+ *     The decode kernels clamp cache lengths to [0, max_seqlen_k].
+ *   - Determinism: the same call on the same inputs gives bitwise identical
+ *     results (fixed reduction order, no floating-point atomics).
+ */
+#ifndef FA355_FA_H
+#define FA355_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum { FA_BF16 = 0, FA_FP16 = 1 } fa_dtype_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, bad window, non-finite scale, misaligned */
+    FA_ERR_UNSUPPORTED = 2,  /* head_dim not in {64, 128}, dtype not bf16/fp16 */
+    FA_ERR_WORKSPACE = 3,    /* decode workspace missing or too small */
+    FA_ERR_HIP = 4           /* the HIP runtime reported an error at launch */
+} fa_status_t;
+
+/* Padded batch (flash_attn_func on the skill page, "Workflow 2").
+ *   q, out : [B, Sq, Hq, d]      k, v : [B, Sk, Hkv, d]
+ *   lse    : [B, Hq, Sq] fp32, may be NULL (not written then)
+ *   B, Hq, Hkv >= 1, Hq % Hkv == 0; Sq, Sk >= 0 (Sq == 0 enqueues nothing;
+ *   Sk == 0 gives O = 0 and LSE = -inf); d in {64, 128};
+ *   window_left, window_right >= -1. */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                   int causal, int window_left, int window_right, float softmax_scale,
+                   fa_dtype_t dtype, hipStream_t stream);
+
+/* Packed sequences (flash_attn_varlen_func; "The One-Line Change ..." page,
+ * sequence packing).  B sequences; sequence z owns query rows
+ * [cu_seqlens_q[z], cu_seqlens_q[z+1]) and key rows
+ * [cu_seqlens_k[z], cu_seqlens_k[z+1]).
+ *   q, out : [total_q, Hq, d]    k, v : [total_k, Hkv, d]
+ *   lse    : [Hq, total_q] fp32, may be NULL
+ *   cu_seqlens_q, cu_seqlens_k : int32 [B+1] DEVICE arrays (may alias)
+ *   max_seqlen_q, max_seqlen_k : host upper bounds of the per-sequence
+ *   lengths, used only to size the launch grid (rows past a bound are not
+ *   computed, so they must be true bounds).
+ *   total_q = cu_seqlens_q[B] is read by the kernels, never by the host. */
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k,
+                          int total_q, int d,
+                          int causal, int window_left, int window_right, float softmax_scale,
+                          fa_dtype_t dtype, hipStream_t stream);
+
+/* Bytes of fp32 workspace fa_decode_kvcache needs for these sizes
+ * (partial outputs and partial LSEs of every split). */
+size_t fa_decode_workspace_bytes(int B, int Hq, int max_seqlen_k, int d, int split_size);
+
+/* One-token decode against a contiguous KV cache, split along the cache and
+ * merged by the LSE rule (explainer page, step 9 "decoding with a cache" and
+ * "Long context beyond a single GPU": partial results combined with the same
+ * online softmax rule).
+ *   q, out           : [B, 1, Hq, d]
+ *   k_cache, v_cache : [B, Sk_cap, Hkv, d]; the first cache_seqlens[b] rows
+ *                      of sequence b are its keys (they include the token
+ *                      being decoded)
+ *   cache_seqlens    : int32 [B] DEVICE array
+ *   lse              : [B, Hq] fp32, may be NULL
+ *   max_seqlen_k     : host upper bound of cache_seqlens (grid and workspace
+ *                      sizing), 1 <= max_seqlen_k <= Sk_cap; longer lengths
+ *                      are clamped to it
+ *   split_size       : keys per split, a positive multiple of 64
+ *   workspace        : DEVICE scratch of at least
+ *                      fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d,
+ *                      split_size) bytes, owned by the caller; contents on
+ *                      entry are ignored.
+ * Two kernels are enqueued on `stream` (split, then combine). */
+fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* cache_seqlens, void* out, float* lse,
+                              int B, int Hq, int Hkv, int Sk_cap, int max_seqlen_k, int d,
+                              int causal, int window_left, int window_right,
+                              float softmax_scale, int split_size,
+                              void* workspace, size_t workspace_bytes,
+                              fa_dtype_t dtype, hipStream_t stream);
+
+/* Static text of a status code. */
+const char* fa_status_str(fa_status_t s);
+
+/* Detail of the calling thread's last non-OK return ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_FA_H */
