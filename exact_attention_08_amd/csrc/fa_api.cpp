@@ -60,7 +60,10 @@ fa_status_t check_common(const void* q, const void* k, const void* v, const void
 void set_scale(float scale, float* c, uint32_t* qsign) {
     // scores are scaled in fp32 inside the exponent; a negative scale is
     // folded into an exact sign flip of q so that c >= 0.
-    *c = std::fabs(scale) * fa::kLog2e_host;
+    // c is kept >= FLT_MIN: masked scores are -inf and -inf * c must stay
+    // -inf; at scale 0 every exp2 argument is then |s|*FLT_MIN ~ 0, so the
+    // weights are exactly uniform in fp32, as scale 0 requires.
+    *c = std::fmax(std::fabs(scale) * fa::kLog2e_host, 1.17549435e-38f);
     *qsign = scale < 0.f ? 0x80008000u : 0u;
 }
 
@@ -70,6 +73,16 @@ fa_status_t launch_status(hipError_t e) {
 }
 
 constexpr long long kMaxGridThreads = (1ll << 32) - 1;
+
+// Buffer loads address one sequence of one tensor with 32-bit byte offsets.
+constexpr long long kMaxSeqBytes = (1ll << 31) - 1;
+
+fa_status_t check_seq_bytes(long long rows, int heads, int d, const char* what) {
+    if (rows * heads * d * 2 > kMaxSeqBytes)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %lld rows x %d heads x %d exceeds 2 GiB per sequence",
+                    what, rows, heads, d);
+    return FA_OK;
+}
 
 }  // namespace
 
@@ -83,6 +96,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     if (st != FA_OK) return st;
     if (Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARG, "Sq, Sk must be >= 0 (got %d, %d)", Sq, Sk);
     if (Sq == 0) return ok();
+    if ((st = check_seq_bytes(Sq, Hq, d, "q")) != FA_OK) return st;
+    if ((st = check_seq_bytes(Sk, Hkv, d, "k/v")) != FA_OK) return st;
     fa::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
     p.cu_q = nullptr; p.cu_k = nullptr;
@@ -116,6 +131,8 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out
     if (max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0)
         return fail(FA_ERR_INVALID_ARG, "max_seqlen_q, max_seqlen_k, total_q must be >= 0");
     if (max_seqlen_q == 0 || total_q == 0) return ok();
+    if ((st = check_seq_bytes(max_seqlen_q, Hq, d, "q")) != FA_OK) return st;
+    if ((st = check_seq_bytes(max_seqlen_k, Hkv, d, "k/v")) != FA_OK) return st;
     fa::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
     p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
@@ -157,6 +174,7 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
     if (split_size < 64 || split_size % 64 != 0)
         return fail(FA_ERR_INVALID_ARG, "split_size must be a positive multiple of 64 (got %d)",
                     split_size);
+    if ((st = check_seq_bytes(Sk_cap, Hkv, d, "k/v cache")) != FA_OK) return st;
     const size_t need = fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d, split_size);
     if (!workspace || !aligned16(workspace))
         return fail(FA_ERR_WORKSPACE, "workspace must be non-null and 16-byte aligned");

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
     }
 
     // key (within a 32-key block) of reduction slot sl of step kk for half g
-    auto slot_key = [&](int kk, int sl) {
+    auto slot_key = [&](int kk, int sl) __attribute__((always_inline)) {
         return 16 * kk + (sl < 4 ? 4 * g + sl : 8 + 4 * g + (sl - 4));
     };
 
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
         u32x4 k[KS];
         vec_t v[16];
     };
-    auto load_block = [&](Block& blk, int jb) {
+    auto load_block = [&](Block& blk, int jb) __attribute__((always_inline)) {
         const int jk = jb + lq;
         const bool kin = jk >= ka && jk < kb;
         const uint16_t* krow = kseq + (long long)jk * tok_stride + g * (D / 2);
@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
     float m_run = -INFINITY, l_run = 0.f;
     const float c = p.c;
 
-    auto process = [&](const Block& cur, int jb) {
+    auto process = [&](const Block& cur, int jb) __attribute__((always_inline)) {
         f32x16 s;
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
@@ -134,6 +134,7 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
         // max are multiplied by exactly 1.
         const bool raise = m_new > m_run + kDecodeRescaleThreshold;
         if (wave_any(raise)) {
+            asm volatile("");   // keep this rare block a real branch (not speculated)
             const float alpha = raise ? exp2_fast(m_run - m_new) : 1.f;
             l_run *= alpha;
 #pragma unroll

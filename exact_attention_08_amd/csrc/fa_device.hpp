@@ -80,4 +80,12 @@ __device__ __forceinline__ void st_global8(void* p, u32x2 v) {
     *reinterpret_cast<u32x2*>(p) = v;
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane i writes
+// lds_base + 16*i (lds_base is wave-uniform); out-of-range offsets write zeros.
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
+                                             int voffset, int soffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, voffset, soffset, 0, 0);
+}
+
 }  // namespace fa

@@ -1,65 +1,111 @@
 // fa_fwd.hip -- fused exact-attention forward for gfx950 (padded and packed).
 //
-// One work-group = 4 waves = 128 query rows of one (sequence, query head);
-// each wave owns 32 rows.  The key axis is walked in tiles of BN keys
-// (64 for d=128, 128 for d=64): the "FlashAttention" explainer page, steps 1-4
-// (tile, score the tile on chip, online softmax, accumulate and normalise
-// once), step 5 (the per-row LSE), step 6 (whole tiles outside the causal /
-// window band are skipped, only boundary tiles are masked element-wise),
-// step 7 (work-groups over query tiles x heads x batch) and step 8 (16-bit
-// MFMA operands, fp32 accumulators and fp32 softmax statistics).
+// The method: the "FlashAttention" explainer page, steps 1-4 (tile the
+// sequence axis, score a tile on chip, online softmax with running max and
+// running sum, accumulate P.V and normalise once), step 5 (the per-row LSE),
+// step 6 (tiles outside the causal / window band are skipped; only boundary
+// tiles are masked element by element), step 7 (work-groups over query tiles
+// x heads x batch) and step 8 (16-bit MFMA operands, fp32 accumulators and
+// fp32 softmax statistics).
+//
+// Work decomposition.  One work-group = 256 query rows of one (sequence,
+// query head), 8 waves of 32 rows (two waves per SIMD, so one wave's MFMAs
+// overlap the other's softmax).  The key axis is walked in tiles of 32 keys.
 //
 // Orientation.  Scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16: the A operand is a 32-key slice of K read from LDS,
-// the B operand is the wave's 32 query rows (kept in registers for the whole
-// kernel).  In the accumulator each lane then holds ONE query row and 16 keys
-// of it, so the row max and row sum are in-lane reductions plus a single
-// exchange with lane l^32.  The probabilities are already in the B-operand
-// layout of the second product O^T = V^T P^T, so P never leaves registers.
-// V is stored transposed in LDS (V^T, written once per tile by the staging
-// threads), so the A operand of the second product is one 16-byte LDS read.
+// the B operand is a 32-row query block held in registers for the whole
+// kernel.  In the accumulator each lane holds ONE query row and 16 keys of
+// it, so the row max and row sum are in-lane reductions plus one exchange
+// with lane l^32, and the probabilities are already in the B-operand layout
+// of the second product O^T = V^T P^T: P never leaves registers.
+//
+// Data movement.  K and V tiles go from HBM/L2 straight into LDS with
+// bounds-checked buffer loads (buffer_load_dwordx4 ... lds): rows past the
+// end of a sequence read as zeros, no staging registers, no branches.  Each
+// lane of such a load picks its own 16-byte source chunk, so the tiles are
+// laid out in LDS in MFMA-operand order rather than row-major:
+//   * K: unit (ks, half, key) holds d-chunk 2*ks+half of that key, so the
+//     A operand of reduction step ks is one contiguous 1 KB wave read
+//     (ds_read_b128 at lane*16);
+//   * V: 8-byte slot (kk, h, db, lane) holds the four columns that lane
+//     contributes to the gfx950 transpose read ds_read_b64_tr_b16 (16 lanes
+//     read a 4-key x 16-column block and each lane receives one column), so
+//     each V^T operand half is one contiguous 512-byte wave read.
+// Contiguous wave reads are bank-conflict free.  K and V are double-buffered
+// in LDS; one barrier per tile.
+//
+// Pipelining.  While the softmax of tile j runs on the VALU, the MFMAs of
+// S(j+1) = K_{j+1} Q^T are already issued; the row max of tile j+1 is taken
+// while the P.V MFMAs of tile j run.
 //
 // Online softmax in base 2: scores are scaled by c = |scale|*log2(e) inside
-// one FMA feeding v_exp_f32.  The running max is only raised when a row's
-// tile max exceeds it by more than 2^8 (exp2 argument 8); until then the
-// stale max is kept, which is exact because the same max is used for the
-// numerator, the sum and the final LSE.  This skips most O rescales.
+// one FMA feeding v_exp_f32.  A row's running max is raised only when its
+// tile max exceeds it by more than 8 (log2 units); until then the stale max
+// is kept, which is exact because the same max is used for the numerator,
+// the sum and the final LSE, and it skips most rescales of O.  O is normalised
+// by the sum of the 16-bit probabilities fed to P.V (v_dot2 against (1, 1)),
+// LSE by the fp32 sum.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
 namespace fa {
 
 template <int D>
-struct FwdTile {
+struct FwdGeo {
+    static constexpr int QB = 1;                // 32-row query blocks per wave
+    static constexpr int WR = 32 * QB;          // rows per wave
     static constexpr int BM = kFwdBM;           // rows per work-group
-    static constexpr int BN = 8192 / D;         // keys per tile
-    static constexpr int NB = BN / 32;          // S^T accumulators (32 keys each)
-    static constexpr int KS = D / 16;           // reduction steps over d
-    static constexpr int DB = D / 32;           // O^T accumulators (32 columns each)
+    static constexpr int NW = BM / WR;          // waves per work-group
+    static constexpr int BN = 32;               // keys per tile
+    static constexpr int KS = D / 16;           // reduction steps over d (= 1 KB K blocks per tile)
+    static constexpr int DB = D / 32;           // O^T accumulators per query block
+    static constexpr int NB = BN / 32;          // S^T accumulators per query block
     static constexpr int KK = BN / 16;          // reduction steps over keys
-    static constexpr int K_STRIDE = D + 8;      // LDS row stride of K (16-bit elements)
-    static constexpr int VT_STRIDE = BN + 8;    // LDS row stride of V^T
-    static constexpr int K_LDS = BN * K_STRIDE;
-    static constexpr int VT_LDS = D * VT_STRIDE;
-    static constexpr int K_CHUNKS = BN * D / 8 / 256;   // 16-byte K chunks per thread
-    static constexpr int DG = D / 4;            // V staging: groups of 4 columns
-    static_assert(K_CHUNKS == 4, "staging assumes 4 K chunks per thread");
-    static_assert((256 / DG) * 8 == BN, "staging assumes 8 keys per thread");
+    static constexpr int VBLK = BN * D * 2 / 1024;   // 1 KB V blocks per tile (= KS)
+    static_assert(BN == 32, "LDS operand layouts assume 32-key tiles");
+    static_assert(VBLK == KS, "K and V tiles have the same number of 1 KB blocks");
+    static_assert(NW * 64 <= 1024, "work-group size");
 };
 
 constexpr float kRescaleThreshold = 8.0f;       // log2 units
+constexpr int kFwdThreads = 512;                // 8 waves
+static_assert(FwdGeo<128>::NW * 64 == kFwdThreads && FwdGeo<64>::NW * 64 == kFwdThreads, "block size");
+
+typedef __attribute__((address_space(3))) short lds_short;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(lds_short*)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float dot2_ones(uint32_t packed, float acc) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed),
+                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+    }
+}
 
 template <int D, bool BF16, bool VARLEN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
-    using T = FwdTile<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[T::K_LDS];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_vt[T::VT_LDS];
+    using T = FwdGeo<D>;
+    constexpr int TILE_ELEMS = T::BN * D;
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE_ELEMS];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int lq = lane & 31;          // query column of this lane
+    const int lq = lane & 31;          // query row (within a 32-row block) of this lane
     const int g = lane >> 5;           // half of the wave
 
     // ---- work-group -> (query tile, head, sequence) ----------------------
@@ -104,8 +150,8 @@ void fa_fwd_kernel(FwdParams p) {
     const int causal = p.causal, wl = p.wl, wr = p.wr;
 
     // visible key interval [lo(i), hi(i)] of query row i (both nondecreasing in i)
-    auto lo_of = [&](int i) { return wl >= 0 ? max(0, i + delta - wl) : 0; };
-    auto hi_of = [&](int i) {
+    auto lo_of = [&](int i) __attribute__((always_inline)) { return wl >= 0 ? max(0, i + delta - wl) : 0; };
+    auto hi_of = [&](int i) __attribute__((always_inline)) {
         int h = sk - 1;
         if (causal) h = min(h, i + delta);
         if (wr >= 0) h = min(h, i + delta + wr);
@@ -115,203 +161,280 @@ void fa_fwd_kernel(FwdParams p) {
     const int wg_last = min(q0 + T::BM, sq) - 1;
     const int kv_lo = lo_of(q0), kv_hi = hi_of(wg_last);
     const int tile_lo = kv_lo / T::BN;
-    const int tile_hi = kv_hi >= kv_lo ? kv_hi / T::BN : tile_lo - 1;
+    const int ntiles = kv_hi >= kv_lo ? kv_hi / T::BN - tile_lo + 1 : 0;
 
     // this wave's rows and key bounds
-    const int r0 = q0 + 32 * wave;
+    const int r0 = q0 + T::WR * wave;
     const bool wave_active = r0 < sq;
-    const int r1 = min(r0 + 31, sq - 1);
+    const int r1 = min(r0 + T::WR - 1, sq - 1);
     const int w_lo = lo_of(r0), w_hi = wave_active ? hi_of(r1) : -1;
     const int int_lo = lo_of(r1), int_hi = hi_of(r0);   // keys every row of the wave sees
-
-    const uint16_t* kbase = (const uint16_t*)p.k + k_tok0 * p.kv_tok_stride + (long long)hkv * D;
-    const uint16_t* vbase = (const uint16_t*)p.v + k_tok0 * p.kv_tok_stride + (long long)hkv * D;
-
-    // ---- staging registers: one K/V tile in flight -----------------------
-    u32x4 kreg[T::K_CHUNKS];
-    u32x2 vreg[8];
-    const int v_dg = tid % T::DG;              // columns 4*v_dg .. +3
-    const int v_kg = tid / T::DG;              // LDS key positions 8*v_kg .. +7
-    auto vkey = [&](int pidx) {                // key (within the tile) at LDS position
-        const int grp16 = v_kg >> 1, gg = v_kg & 1;
-        return 16 * grp16 + (pidx < 4 ? 4 * gg + pidx : 8 + 4 * gg + (pidx - 4));
+    auto part = [&](int jt) __attribute__((always_inline)) {                  // wave has a visible key in tile jt
+        return wave_active && jt * T::BN <= w_hi && jt * T::BN + T::BN - 1 >= w_lo;
+    };
+    auto interior = [&](int jt) __attribute__((always_inline)) {              // every row of the wave sees every key of jt
+        return jt * T::BN >= int_lo && jt * T::BN + T::BN - 1 <= int_hi;
     };
 
-    auto load_tile = [&](int jt) {
-        const int j0 = jt * T::BN;
+    // ---- buffer resources ------------------------------------------------
+    const long long tok_bytes_kv = p.kv_tok_stride * 2;
+    const long long tok_bytes_q = p.q_tok_stride * 2;
+    const char* kseq = (const char*)p.k + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
+    const char* vseq = (const char*)p.v + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
+    auto tile_rsrc = [&](const char* base, int jt) __attribute__((always_inline)) {
+        const int rows_left = max(sk - jt * T::BN, 0);
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base + (long long)jt * T::BN * tok_bytes_kv), (short)0,
+            (int)(rows_left * tok_bytes_kv), 0x00020000);
+    };
+    // 1 KB LDS blocks of a tile and their per-lane sources.  K block ks, lane
+    // L: key L%32, d-chunk 2*ks + L/32.  V block b, 16-byte unit u = 64*b + L:
+    // blk = u/32 = (2*kk + h)*DB + db, r = u%32 -> key 16*kk + 8*h + 4*(r/16)
+    // + (r/2)%4, d-chunk 4*db + 2*((r/8)%2) + r%2.  K block b is loaded by wave
+    // b % NW, V block b by wave (b + KS) % NW.
+    const int k_src = (lane & 31) * (int)tok_bytes_kv + (lane >> 5) * 16;
+    auto v_src = [&](int vb) __attribute__((always_inline)) {
+        const int u = vb * 64 + lane;
+        const int blk = u >> 5, r = u & 31;
+        const int db = blk % T::DB, kh = blk / T::DB;
+        const int row = 8 * kh + 4 * (r >> 4) + ((r >> 1) & 3);
+        const int chunk = 4 * db + 2 * ((r >> 3) & 1) + (r & 1);
+        return row * (int)tok_bytes_kv + chunk * 16;
+    };
+    auto load_k = [&](uint16_t* dst, int jt) __attribute__((always_inline)) {
+        const auto rs = tile_rsrc(kseq, jt);
 #pragma unroll
-        for (int c = 0; c < T::K_CHUNKS; ++c) {
-            const int chunk = tid + 256 * c;
-            const int row = chunk / (D / 8), col = chunk % (D / 8);
-            const int j = j0 + row;
-            kreg[c] = j < sk ? ld_global16(kbase + (long long)j * p.kv_tok_stride + col * 8)
-                             : (u32x4){0u, 0u, 0u, 0u};
-        }
+        for (int kb = 0; kb < T::KS; ++kb)
+            if (kb % T::NW == wave)
+                dma16_to_lds(rs, dst + kb * 512, k_src, kb * 32);
+    };
+    auto load_v = [&](uint16_t* dst, int jt) __attribute__((always_inline)) {
+        const auto rs = tile_rsrc(vseq, jt);
 #pragma unroll
-        for (int pi = 0; pi < 8; ++pi) {
-            const int j = j0 + vkey(pi);
-            vreg[pi] = j < sk ? ld_global8(vbase + (long long)j * p.kv_tok_stride + v_dg * 4)
-                              : (u32x2){0u, 0u};
-        }
+        for (int vb = 0; vb < T::VBLK; ++vb)
+            if ((vb + T::KS) % T::NW == wave)
+                dma16_to_lds(rs, dst + vb * 512, v_src(vb), 0);
     };
 
-    auto store_tile = [&]() {
+    // ---- query blocks as MFMA B operands ---------------------------------
+    u32x4 qreg[T::QB][T::KS];
+    {
+        const auto qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const char*)p.q + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2),
+            (short)0, (int)(sq * tok_bytes_q), 0x00020000);
 #pragma unroll
-        for (int c = 0; c < T::K_CHUNKS; ++c) {
-            const int chunk = tid + 256 * c;
-            const int row = chunk / (D / 8), col = chunk % (D / 8);
-            *reinterpret_cast<u32x4*>(&lds_k[row * T::K_STRIDE + col * 8]) = kreg[c];
-        }
-        // transpose 8 keys x 4 columns into 4 rows of V^T (8 keys each)
+        for (int qb = 0; qb < T::QB; ++qb)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-            u32x4 w;
-#pragma unroll
-            for (int p2 = 0; p2 < 4; ++p2) {
-                const uint32_t a = (cc >> 1) ? vreg[2 * p2].y : vreg[2 * p2].x;
-                const uint32_t bb = (cc >> 1) ? vreg[2 * p2 + 1].y : vreg[2 * p2 + 1].x;
-                w[p2] = (cc & 1) ? ((a >> 16) | (bb & 0xffff0000u))
-                                 : ((a & 0xffffu) | (bb << 16));
+            for (int ks = 0; ks < T::KS; ++ks) {
+                const int row = r0 + 32 * qb + lq;
+                u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+                    qrs, (int)(row * tok_bytes_q) + (16 * ks + 8 * g) * 2, 0, 0);
+                qreg[qb][ks] = x ^ p.qsign;    // exact negation when scale < 0
             }
-            *reinterpret_cast<u32x4*>(&lds_vt[(4 * v_dg + cc) * T::VT_STRIDE + v_kg * 8]) = w;
-        }
-    };
-
-    if (tile_lo <= tile_hi) {
-        load_tile(tile_lo);
-        store_tile();
     }
 
-    // ---- the wave's 32 query rows as MFMA B operands ---------------------
-    const int my_row = r0 + lq;
-    const uint16_t* qrow = (const uint16_t*)p.q + (q_tok0 + my_row) * p.q_tok_stride +
-                           (long long)hq * D;
-    u32x4 qreg[T::KS];
+    f32x16 oacc[T::QB][T::DB];
 #pragma unroll
-    for (int ks = 0; ks < T::KS; ++ks) {
-        u32x4 x = my_row < sq ? ld_global16(qrow + ks * 16 + g * 8) : (u32x4){0u, 0u, 0u, 0u};
-        qreg[ks] = x ^ p.qsign;                // exact negation when scale < 0
-    }
-
-    f32x16 oacc[T::DB];
+    for (int qb = 0; qb < T::QB; ++qb)
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
-        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-    float m_run = -INFINITY;                   // running max of scaled scores (log2 units)
-    float l_run = 0.f;                         // this lane's share of the running sum
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[qb][db][e] = 0.f;
+    // running max (log2 units) and this lane's share of the fp32 / 16-bit-rounded sums
+    float m_run[T::QB], l_run[T::QB], lr_run[T::QB];
+#pragma unroll
+    for (int qb = 0; qb < T::QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; lr_run[qb] = 0.f; }
     const float c = p.c;
 
-    // per-lane visible interval, relative to the lane's first key offset 4*g
-    const int my_pos = my_row + delta;
-    int my_lo = wl >= 0 ? my_pos - wl : -0x40000000;
-    int my_hi = sk - 1;
-    if (causal) my_hi = min(my_hi, my_pos);
-    if (wr >= 0) my_hi = min(my_hi, my_pos + wr);
-
-    for (int jt = tile_lo; jt <= tile_hi; ++jt) {
-        __syncthreads();                       // tile jt is in LDS
-        if (jt < tile_hi) load_tile(jt + 1);   // next tile in flight during compute
-
-        const int j0 = jt * T::BN;
-        const int j1 = j0 + T::BN - 1;
-        if (wave_active && j0 <= w_hi && j1 >= w_lo) {
-            // S^T = K Q^T
-            f32x16 s[T::NB];
+    // per-lane visible interval of each query block, relative to its first key 4*g
+    int rel_lo[T::QB], rel_hi[T::QB];
 #pragma unroll
-            for (int nb = 0; nb < T::NB; ++nb) {
-                for (int e = 0; e < 16; ++e) s[nb][e] = 0.f;
+    for (int qb = 0; qb < T::QB; ++qb) {
+        const int pos = r0 + 32 * qb + lq + delta;
+        rel_lo[qb] = (wl >= 0 ? pos - wl : -0x40000000) - 4 * g;
+        int h = sk - 1;
+        if (causal) h = min(h, pos);
+        if (wr >= 0) h = min(h, pos + wr);
+        rel_hi[qb] = h - 4 * g;
+    }
+
+    f32x16 sacc[2][T::QB][T::NB];              // [parity][query block][key block]
+    u32x4 pb[T::QB][T::KK];                    // P as 16-bit B operands
+
+    // ---- phases ----------------------------------------------------------
+    auto qk = [&](f32x16 (&s)[T::QB][T::NB], const uint16_t* kt) __attribute__((always_inline)) {
 #pragma unroll
-                for (int ks = 0; ks < T::KS; ++ks) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        &lds_k[(32 * nb + lq) * T::K_STRIDE + ks * 16 + g * 8]);
-                    s[nb] = mfma32x32x16<BF16>(a, qreg[ks], s[nb]);
-                }
+        for (int qb = 0; qb < T::QB; ++qb)
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[qb][nb][e] = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(kt + ks * 512 + lane * 8);
+#pragma unroll
+                for (int qb = 0; qb < T::QB; ++qb)
+                    s[qb][nb] = mfma32x32x16<BF16>(a, qreg[qb][ks], s[qb][nb]);
             }
-
-            const bool masked = !(j0 >= int_lo && j1 <= int_hi);
-            // key of element e in block nb: j0 + 32*nb + 8*(e>>2) + 4*g + (e&3)
-            const int rel_lo = my_lo - j0 - 4 * g;
-            const int rel_hi = my_hi - j0 - 4 * g;
-
+    };
+    // row max of a tile (masking it first when needed) and the lazy rescale
+    auto rowmax = [&](f32x16 (&s)[T::QB][T::NB], int jt, bool masked) __attribute__((always_inline)) {
+        float mnew[T::QB];
+        bool raise[T::QB];
+        bool any_raise = false;
+#pragma unroll
+        for (int qb = 0; qb < T::QB; ++qb) {
+            if (masked) {
+                const int lo = rel_lo[qb] - jt * T::BN, hi = rel_hi[qb] - jt * T::BN;
+#pragma unroll
+                for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int off = 32 * nb + 8 * (e >> 2) + (e & 3);
+                        s[qb][nb][e] = (off >= lo && off <= hi) ? s[qb][nb][e] : -INFINITY;
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int off = 32 * nb + 8 * (e >> 2) + (e & 3);
-                    const bool vis = !masked || (off >= rel_lo && off <= rel_hi);
-                    mx = fmaxf(mx, vis ? s[nb][e] : -INFINITY);
-                }
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][nb][e]);
             mx = fmaxf(mx, xor32(mx));
-            const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
-            const float m_new = fmaxf(m_run, m_tile);
-            // Per-row decision (rows are independent); the branch only skips
-            // the work when no row of the wave needs it.  Rows that keep their
-            // max are multiplied by exactly 1.
-            const bool raise = m_new > m_run + kRescaleThreshold;
-            if (wave_any(raise)) {
-                const float alpha = raise ? exp2_fast(m_run - m_new) : 1.f;
-                l_run *= alpha;
+            mnew[qb] = fmaxf(m_run[qb], mx * c);      // -inf stays -inf (c > 0)
+            raise[qb] = mnew[qb] > m_run[qb] + kRescaleThreshold;
+            any_raise = any_raise || raise[qb];
+        }
+        // Per-row decision (rows are independent); the branch only skips the
+        // work when no row of the wave needs it.  Rows keeping their max are
+        // multiplied by exactly 1.
+        if (wave_any(any_raise)) {
+            asm volatile("");   // keep this rare block a real branch (not speculated)
+#pragma unroll
+            for (int qb = 0; qb < T::QB; ++qb) {
+                const float alpha = raise[qb] ? exp2_fast(m_run[qb] - mnew[qb]) : 1.f;
+                l_run[qb] *= alpha;
+                lr_run[qb] *= alpha;
 #pragma unroll
                 for (int db = 0; db < T::DB; ++db)
-                    for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-                m_run = raise ? m_new : m_run;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
+                m_run[qb] = raise[qb] ? mnew[qb] : m_run[qb];
             }
-            const float m_use = m_run == -INFINITY ? 0.f : m_run;
-
-            // P = exp2(S*c - m), packed to 16-bit B operands of O^T = V^T P^T
-            u32x4 pb[T::KK];
+        }
+    };
+    // P = exp2(S*c - m) as 16-bit B operands; masked scores are -inf -> 0
+    auto softmax_exp = [&](f32x16 (&s)[T::QB][T::NB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < T::QB; ++qb) {
+            const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
 #pragma unroll
             for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
                 for (int e = 0; e < 16; e += 2) {
-                    float pv[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int ee = e + u;
-                        const int off = 32 * nb + 8 * (ee >> 2) + (ee & 3);
-                        const bool vis = !masked || (off >= rel_lo && off <= rel_hi);
-                        const float x = exp2_fast(fmaf(s[nb][ee], c, -m_use));
-                        pv[u] = vis ? x : 0.f;
-                        l_run += pv[u];
-                    }
-                    // element e of block nb is slot (e & 7) of reduction step 2*nb + (e >> 3)
-                    pb[2 * nb + (e >> 3)][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
-                }
-
-            // O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                for (int kk = 0; kk < T::KK; ++kk) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(
-                        &lds_vt[(32 * db + lq) * T::VT_STRIDE + kk * 16 + g * 8]);
-                    oacc[db] = mfma32x32x16<BF16>(a, pb[kk], oacc[db]);
+                    const float x0 = exp2_fast(fmaf(s[qb][nb][e], c, -m_use));
+                    const float x1 = exp2_fast(fmaf(s[qb][nb][e + 1], c, -m_use));
+                    const uint32_t pk = pack2<BF16>(x0, x1);
+                    // element e of key block nb is slot (e & 7) of reduction step 2*nb + (e >> 3)
+                    pb[qb][2 * nb + (e >> 3)][(e & 7) >> 1] = pk;
+                    // two normalisers: O is divided by the sum of the 16-bit weights
+                    // actually fed to P.V (so its weights sum to one); LSE uses the sum
+                    // of the fp32 values (16-bit rounding would bias it by up to 2^-9)
+                    l_run[qb] += x0 + x1;
+                    lr_run[qb] = dot2_ones<BF16>(pk, lr_run[qb]);
                 }
         }
-        __syncthreads();                       // every wave is done with tile jt
-        if (jt < tile_hi) store_tile();
+    };
+    auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int kk = 0; kk < T::KK; ++kk) {
+                const uint16_t* base = vt + ((2 * kk) * T::DB + db) * 256 + lane * 4;
+                const u32x2 lo = ds_read_tr16(base);                    // keys 16kk + 4g + 0..3
+                const u32x2 hi = ds_read_tr16(base + T::DB * 256);      // keys 16kk + 8 + 4g + 0..3
+                const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+                for (int qb = 0; qb < T::QB; ++qb)
+                    oacc[qb][db] = mfma32x32x16<BF16>(a, pb[qb][kk], oacc[qb][db]);
+            }
+    };
+    auto sync_tile = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    // One tile step.  On entry tile j's scores (scur) carry their final row
+    // max; K_{j+1} is in k_next and V_j in v_cur.  Loads V_{j+1} into v_free
+    // and K_{j+2} into k_free; the scores of tile j+1 go to snext.
+    auto step = [&](uint16_t* k_next, uint16_t* k_free, const uint16_t* v_cur, uint16_t* v_free,
+                    f32x16 (&scur)[T::QB][T::NB], f32x16 (&snext)[T::QB][T::NB], int j)
+        __attribute__((always_inline)) {
+        const int jend = tile_lo + ntiles - 1;
+        if (j + 1 <= jend) load_v(v_free, j + 1);
+        if (j + 2 <= jend) load_k(k_free, j + 2);
+        const bool has_next = j + 1 <= jend;
+        const bool pj = part(j), pn = has_next && part(j + 1);
+        if (pj && pn && interior(j + 1)) {
+            // steady state: one straight-line block
+            qk(snext, k_next);
+            softmax_exp(scur);
+            pv(v_cur);
+            rowmax(snext, j + 1, false);
+        } else {
+            if (pn) qk(snext, k_next);
+            if (pj) {
+                softmax_exp(scur);
+                pv(v_cur);
+            }
+            if (pn) rowmax(snext, j + 1, !interior(j + 1));
+        }
+        sync_tile();
+    };
+
+    if (ntiles > 0) {
+        load_k(k_lds0, tile_lo);
+        load_v(v_lds0, tile_lo);
+        if (ntiles > 1) load_k(k_lds1, tile_lo + 1);
+        sync_tile();
+        if (part(tile_lo)) {
+            qk(sacc[0], k_lds0);
+            rowmax(sacc[0], tile_lo, !interior(tile_lo));
+        }
+        // unrolled by two so that every LDS buffer reference is static
+        for (int r = 0; r < ntiles; r += 2) {
+            step(k_lds1, k_lds0, v_lds0, v_lds1, sacc[0], sacc[1], tile_lo + r);
+            if (r + 1 >= ntiles) break;
+            step(k_lds0, k_lds1, v_lds1, v_lds0, sacc[1], sacc[0], tile_lo + r + 1);
+        }
     }
 
     // ---- epilogue: normalise once, write O and LSE -----------------------
-    const float l_tot = l_run + xor32(l_run);
-    if (my_row < sq) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* orow = (uint16_t*)p.o + (q_tok0 + my_row) * p.q_tok_stride + (long long)hq * D;
+    const auto ors = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((char*)p.o + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2), (short)0,
+        (int)(sq * tok_bytes_q), 0x00020000);
+#pragma unroll
+    for (int qb = 0; qb < T::QB; ++qb) {
+        const float l_tot = l_run[qb] + xor32(l_run[qb]);
+        const float lr_tot = lr_run[qb] + xor32(lr_run[qb]);
+        const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+        const int row = r0 + 32 * qb + lq;
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 u32x2 w;
-                w.x = pack2<BF16>(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-                w.y = pack2<BF16>(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
-                st_global8(orow + 32 * db + 8 * jj + 4 * g, w);
+                w.x = pack2<BF16>(oacc[qb][db][4 * jj + 0] * inv, oacc[qb][db][4 * jj + 1] * inv);
+                w.y = pack2<BF16>(oacc[qb][db][4 * jj + 2] * inv, oacc[qb][db][4 * jj + 3] * inv);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    w, ors, (int)(row * tok_bytes_q) + (32 * db + 8 * jj + 4 * g) * 2, 0, 0);
             }
-        if (p.lse != nullptr && g == 0) {
+        if (p.lse != nullptr && g == 0 && row < sq) {
             const long long row_base = VARLEN ? q_tok0 : 0;
-            const float lse = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
-            p.lse[(long long)b * p.lse_b_stride + (long long)hq * p.lse_h_stride + row_base +
-                  my_row] = lse;
+            const float lse = l_tot > 0.f ? (m_run[qb] + log2_fast(l_tot)) * kLn2 : -INFINITY;
+            p.lse[(long long)b * p.lse_b_stride + (long long)hq * p.lse_h_stride + row_base + row] =
+                lse;
         }
     }
 }
@@ -320,8 +443,8 @@ template <int D, bool BF16, bool VARLEN>
 static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
     const long long nblocks = (long long)p.nqt * p.Hq * p.B;
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN>), dim3((unsigned)nblocks), dim3(256), 0, s,
-                       p);
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN>), dim3((unsigned)nblocks),
+                       dim3(kFwdThreads), 0, s, p);
     return hipGetLastError();
 }
 
