@@ -80,12 +80,34 @@ __device__ __forceinline__ void st_global8(void* p, u32x2 v) {
     *reinterpret_cast<u32x2*>(p) = v;
 }
 
-// 16 bytes per lane from a buffer straight into LDS: lane i writes
-// lds_base + 16*i (lds_base is wave-uniform); out-of-range offsets write zeros.
-__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
-                                             int voffset, int soffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void*)(lds_base), 16, voffset, soffset, 0, 0);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource for raw (stride 0) 32-bit-offset loads/stores of [base,
+// base + num_bytes); out-of-range loads return zeros, stores are dropped.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int num_bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return (i32x4){(int)(uint32_t)a, (int)(uint32_t)(a >> 32), num_bytes, 0x00020000};
+}
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)(p);
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane i writes lds_base + 16*i, lds_base wave-uniform; out-of-range
+// offsets write zeros.  Written as inline asm so that the compiler does not
+// track it: the instruction has no destination registers, and the caller
+// waits for it explicitly (s_waitcnt vmcnt) before reading the LDS it fills.
+__device__ __forceinline__ void dma16_to_lds(i32x4 rsrc, uint32_t lds_base, int voffset,
+                                             int soffset) {
+    asm volatile(
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %0, %1, %2 offen lds"
+        :
+        : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(lds_base)
+        : "memory", "m0");
 }
 
 }  // namespace fa

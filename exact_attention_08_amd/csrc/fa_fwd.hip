@@ -32,8 +32,9 @@
 //     contributes to the gfx950 transpose read ds_read_b64_tr_b16 (16 lanes
 //     read a 4-key x 16-column block and each lane receives one column), so
 //     each V^T operand half is one contiguous 512-byte wave read.
-// Contiguous wave reads are bank-conflict free.  K and V are double-buffered
-// in LDS; one barrier per tile.
+// Contiguous wave reads are bank-conflict free.  K and V are buffered in LDS
+// in a ring of STAGES tiles each, so loads are issued STAGES-1 tiles ahead of
+// use; one barrier per tile.
 //
 // Pipelining.  While the softmax of tile j runs on the VALU, the MFMAs of
 // S(j+1) = K_{j+1} Q^T are already issued; the row max of tile j+1 is taken
@@ -63,9 +64,12 @@ struct FwdGeo {
     static constexpr int NB = BN / 32;          // S^T accumulators per query block
     static constexpr int KK = BN / 16;          // reduction steps over keys
     static constexpr int VBLK = BN * D * 2 / 1024;   // 1 KB V blocks per tile (= KS)
+    static constexpr int STAGES = 6;            // LDS ring depth (tiles of K and of V)
+    static constexpr int LPS = 2 * KS / NW;     // DMA loads per wave per tile step
     static_assert(BN == 32, "LDS operand layouts assume 32-key tiles");
     static_assert(VBLK == KS, "K and V tiles have the same number of 1 KB blocks");
     static_assert(NW * 64 <= 1024, "work-group size");
+    static_assert(LPS * NW == 2 * KS, "every wave issues the same number of loads per step");
 };
 
 constexpr float kRescaleThreshold = 8.0f;       // log2 units
@@ -97,10 +101,8 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 
 void fa_fwd_kernel(FwdParams p) {
     using T = FwdGeo<D>;
     constexpr int TILE_ELEMS = T::BN * D;
-    __shared__ __attribute__((aligned(1024))) uint16_t k_lds0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t k_lds1[TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_lds0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_lds1[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t k_ring[T::STAGES * TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_ring[T::STAGES * TILE_ELEMS];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -162,6 +164,7 @@ void fa_fwd_kernel(FwdParams p) {
     const int kv_lo = lo_of(q0), kv_hi = hi_of(wg_last);
     const int tile_lo = kv_lo / T::BN;
     const int ntiles = kv_hi >= kv_lo ? kv_hi / T::BN - tile_lo + 1 : 0;
+    const int tile_last = tile_lo + ntiles - 1;
 
     // this wave's rows and key bounds
     const int r0 = q0 + T::WR * wave;
@@ -181,47 +184,49 @@ void fa_fwd_kernel(FwdParams p) {
     const long long tok_bytes_q = p.q_tok_stride * 2;
     const char* kseq = (const char*)p.k + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
     const char* vseq = (const char*)p.v + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
+    // tiles outside [tile_lo, tile_last] get zero records: their loads write
+    // zeros to LDS without touching memory (keeps per-step load counts fixed)
     auto tile_rsrc = [&](const char* base, int jt) __attribute__((always_inline)) {
-        const int rows_left = max(sk - jt * T::BN, 0);
-        return __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base + (long long)jt * T::BN * tok_bytes_kv), (short)0,
-            (int)(rows_left * tok_bytes_kv), 0x00020000);
+        const bool valid = jt >= tile_lo && jt <= tile_last;
+        const int rows_left = valid ? max(sk - jt * T::BN, 0) : 0;
+        return make_rsrc(base + (long long)jt * T::BN * tok_bytes_kv,
+                         (int)(rows_left * tok_bytes_kv));
     };
     // 1 KB LDS blocks of a tile and their per-lane sources.  K block ks, lane
     // L: key L%32, d-chunk 2*ks + L/32.  V block b, 16-byte unit u = 64*b + L:
     // blk = u/32 = (2*kk + h)*DB + db, r = u%32 -> key 16*kk + 8*h + 4*(r/16)
-    // + (r/2)%4, d-chunk 4*db + 2*((r/8)%2) + r%2.  K block b is loaded by wave
-    // b % NW, V block b by wave (b + KS) % NW.
-    const int k_src = (lane & 31) * (int)tok_bytes_kv + (lane >> 5) * 16;
-    auto v_src = [&](int vb) __attribute__((always_inline)) {
-        const int u = vb * 64 + lane;
-        const int blk = u >> 5, r = u & 31;
-        const int db = blk % T::DB, kh = blk / T::DB;
-        const int row = 8 * kh + 4 * (r >> 4) + ((r >> 1) & 3);
-        const int chunk = 4 * db + 2 * ((r >> 3) & 1) + (r & 1);
-        return row * (int)tok_bytes_kv + chunk * 16;
-    };
-    auto load_k = [&](uint16_t* dst, int jt) __attribute__((always_inline)) {
-        const auto rs = tile_rsrc(kseq, jt);
+    // + (r/2)%4, d-chunk 4*db + 2*((r/8)%2) + r%2.  The 2*KS blocks of a step
+    // (K blocks, then V blocks) are spread over the waves: wave w issues
+    // blocks w, w + NW, ...
+    int dma_src[T::LPS], dma_soff[T::LPS], dma_dst[T::LPS];
+    bool dma_is_k[T::LPS];
 #pragma unroll
-        for (int kb = 0; kb < T::KS; ++kb)
-            if (kb % T::NW == wave)
-                dma16_to_lds(rs, dst + kb * 512, k_src, kb * 32);
-    };
-    auto load_v = [&](uint16_t* dst, int jt) __attribute__((always_inline)) {
-        const auto rs = tile_rsrc(vseq, jt);
-#pragma unroll
-        for (int vb = 0; vb < T::VBLK; ++vb)
-            if ((vb + T::KS) % T::NW == wave)
-                dma16_to_lds(rs, dst + vb * 512, v_src(vb), 0);
-    };
+    for (int i = 0; i < T::LPS; ++i) {
+        const int gb = wave + i * T::NW;
+        dma_is_k[i] = gb < T::KS;
+        if (dma_is_k[i]) {
+            dma_src[i] = (lane & 31) * (int)tok_bytes_kv + (lane >> 5) * 16;
+            dma_soff[i] = gb * 32;
+            dma_dst[i] = gb * 1024;
+        } else {
+            const int vb = gb - T::KS;
+            const int u = vb * 64 + lane;
+            const int blk = u >> 5, r = u & 31;
+            const int db = blk % T::DB, kh = blk / T::DB;
+            const int row = 8 * kh + 4 * (r >> 4) + ((r >> 1) & 3);
+            const int chunk = 4 * db + 2 * ((r >> 3) & 1) + (r & 1);
+            dma_src[i] = row * (int)tok_bytes_kv + chunk * 16;
+            dma_soff[i] = 0;
+            dma_dst[i] = vb * 1024;
+        }
+    }
 
     // ---- query blocks as MFMA B operands ---------------------------------
     u32x4 qreg[T::QB][T::KS];
     {
         const auto qrs = __builtin_amdgcn_make_buffer_rsrc(
             (void*)((const char*)p.q + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2),
-            (short)0, (int)(sq * tok_bytes_q), 0x00020000);
+            (short)0, (int)(sq * tok_bytes_q), 0x00020000);   // zero rows past the sequence
 #pragma unroll
         for (int qb = 0; qb < T::QB; ++qb)
 #pragma unroll
@@ -360,33 +365,54 @@ void fa_fwd_kernel(FwdParams p) {
                     oacc[qb][db] = mfma32x32x16<BF16>(a, pb[qb][kk], oacc[qb][db]);
             }
     };
+
+    // Ring slot of tile t (t >= tile_lo - 1).
+    auto kslot = [&](int t) __attribute__((always_inline)) {
+        return k_ring + ((t - tile_lo + T::STAGES) % T::STAGES) * TILE_ELEMS;
+    };
+    auto vslot = [&](int t) __attribute__((always_inline)) {
+        return v_ring + ((t - tile_lo + T::STAGES) % T::STAGES) * TILE_ELEMS;
+    };
+    // Load set of step t: K_t and V_{t-1}.  Step j issues set j + STAGES,
+    // which refills the slots of K_j and V_{j-1} (both consumed by step j-1).
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const i32x4 krs = tile_rsrc(kseq, t), vrs = tile_rsrc(vseq, t - 1);
+        const uint32_t kdst = lds_addr(kslot(t)), vdst = lds_addr(vslot(t - 1));
+#pragma unroll
+        for (int i = 0; i < T::LPS; ++i) {
+            if (dma_is_k[i])
+                dma16_to_lds(krs, kdst + dma_dst[i], dma_src[i], dma_soff[i]);
+            else
+                dma16_to_lds(vrs, vdst + dma_dst[i], dma_src[i], dma_soff[i]);
+        }
+    };
+    // Before step j the sets up to j+1 (K_{j+1}, V_j) must have landed in
+    // every wave; the STAGES-2 sets issued after it may still be in flight.
+    // The wait and the barrier form one asm statement so that no LDS access
+    // is moved across them.
     auto sync_tile = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
+                     ::"n"(T::LPS * (T::STAGES - 2)) : "memory");
     };
 
     // One tile step.  On entry tile j's scores (scur) carry their final row
-    // max; K_{j+1} is in k_next and V_j in v_cur.  Loads V_{j+1} into v_free
-    // and K_{j+2} into k_free; the scores of tile j+1 go to snext.
-    auto step = [&](uint16_t* k_next, uint16_t* k_free, const uint16_t* v_cur, uint16_t* v_free,
-                    f32x16 (&scur)[T::QB][T::NB], f32x16 (&snext)[T::QB][T::NB], int j)
+    // max; K_{j+1} and V_j are in the ring.
+    auto step = [&](f32x16 (&scur)[T::QB][T::NB], f32x16 (&snext)[T::QB][T::NB], int j)
         __attribute__((always_inline)) {
-        const int jend = tile_lo + ntiles - 1;
-        if (j + 1 <= jend) load_v(v_free, j + 1);
-        if (j + 2 <= jend) load_k(k_free, j + 2);
-        const bool has_next = j + 1 <= jend;
+        issue(j + T::STAGES);
+        const bool has_next = j + 1 <= tile_last;
         const bool pj = part(j), pn = has_next && part(j + 1);
         if (pj && pn && interior(j + 1)) {
             // steady state: one straight-line block
-            qk(snext, k_next);
+            qk(snext, kslot(j + 1));
             softmax_exp(scur);
-            pv(v_cur);
+            pv(vslot(j));
             rowmax(snext, j + 1, false);
         } else {
-            if (pn) qk(snext, k_next);
+            if (pn) qk(snext, kslot(j + 1));
             if (pj) {
                 softmax_exp(scur);
-                pv(v_cur);
+                pv(vslot(j));
             }
             if (pn) rowmax(snext, j + 1, !interior(j + 1));
         }
@@ -394,21 +420,20 @@ void fa_fwd_kernel(FwdParams p) {
     };
 
     if (ntiles > 0) {
-        load_k(k_lds0, tile_lo);
-        load_v(v_lds0, tile_lo);
-        if (ntiles > 1) load_k(k_lds1, tile_lo + 1);
+        for (int t = tile_lo; t < tile_lo + T::STAGES; ++t) issue(t);
         sync_tile();
         if (part(tile_lo)) {
-            qk(sacc[0], k_lds0);
+            qk(sacc[0], kslot(tile_lo));
             rowmax(sacc[0], tile_lo, !interior(tile_lo));
         }
-        // unrolled by two so that every LDS buffer reference is static
+        // unrolled by two so that the score buffers swap roles statically
         for (int r = 0; r < ntiles; r += 2) {
-            step(k_lds1, k_lds0, v_lds0, v_lds1, sacc[0], sacc[1], tile_lo + r);
+            step(sacc[0], sacc[1], tile_lo + r);
             if (r + 1 >= ntiles) break;
-            step(k_lds0, k_lds1, v_lds1, v_lds0, sacc[1], sacc[0], tile_lo + r + 1);
+            step(sacc[1], sacc[0], tile_lo + r + 1);
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // DMA loads of unused sets still in flight
 
     // ---- epilogue: normalise once, write O and LSE -----------------------
     const auto ors = __builtin_amdgcn_make_buffer_rsrc(
