@@ -54,22 +54,20 @@ namespace fa {
 
 template <int D>
 struct FwdGeo {
-    static constexpr int QB = 1;                // 32-row query blocks per wave
-    static constexpr int WR = 32 * QB;          // rows per wave
+    static constexpr int WR = 32;               // rows per wave (one 32-row query block)
     static constexpr int BM = kFwdBM;           // rows per work-group
     static constexpr int NW = BM / WR;          // waves per work-group
     static constexpr int BN = 32;               // keys per tile
-    static constexpr int KS = D / 16;           // reduction steps over d (= 1 KB K blocks per tile)
-    static constexpr int DB = D / 32;           // O^T accumulators per query block
-    static constexpr int NB = BN / 32;          // S^T accumulators per query block
+    static constexpr int NB = BN / 32;          // S^T accumulators (32 keys each)
+    static constexpr int KS = D / 16;           // reduction steps over d
+    static constexpr int DB = D / 32;           // O^T accumulators (32 columns each)
     static constexpr int KK = BN / 16;          // reduction steps over keys
-    static constexpr int VBLK = BN * D * 2 / 1024;   // 1 KB V blocks per tile (= KS)
-    static constexpr int STAGES = 6;            // LDS ring depth (tiles of K and of V)
-    static constexpr int LPS = 2 * KS / NW;     // DMA loads per wave per tile step
-    static_assert(BN == 32, "LDS operand layouts assume 32-key tiles");
-    static_assert(VBLK == KS, "K and V tiles have the same number of 1 KB blocks");
-    static_assert(NW * 64 <= 1024, "work-group size");
-    static_assert(LPS * NW == 2 * KS, "every wave issues the same number of loads per step");
+    static constexpr int TILE_ELEMS = BN * D;
+    static constexpr int TILE_BLOCKS = TILE_ELEMS * 2 / 1024;   // 1 KB blocks per K (or V) tile
+    static constexpr int STAGES = 8;            // LDS ring depth (power of two)
+    static constexpr int LPS = 2 * TILE_BLOCKS / NW;            // DMA loads per wave per step
+    static_assert((2 * TILE_BLOCKS) % NW == 0, "the blocks of a step split evenly over the waves");
+    static_assert((STAGES & (STAGES - 1)) == 0, "ring depth must be a power of two");
 };
 
 constexpr float kRescaleThreshold = 8.0f;       // log2 units
@@ -100,14 +98,14 @@ template <int D, bool BF16, bool VARLEN>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {
     using T = FwdGeo<D>;
-    constexpr int TILE_ELEMS = T::BN * D;
-    __shared__ __attribute__((aligned(1024))) uint16_t k_ring[T::STAGES * TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_ring[T::STAGES * TILE_ELEMS];
+    constexpr int TE = T::TILE_ELEMS;
+    __shared__ __attribute__((aligned(1024))) uint16_t k_ring[T::STAGES * TE];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_ring[T::STAGES * TE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int lq = lane & 31;          // query row (within a 32-row block) of this lane
+    const int lq = lane & 31;          // query row (within the wave's 32 rows) of this lane
     const int g = lane >> 5;           // half of the wave
 
     // ---- work-group -> (query tile, head, sequence) ----------------------
@@ -152,7 +150,9 @@ void fa_fwd_kernel(FwdParams p) {
     const int causal = p.causal, wl = p.wl, wr = p.wr;
 
     // visible key interval [lo(i), hi(i)] of query row i (both nondecreasing in i)
-    auto lo_of = [&](int i) __attribute__((always_inline)) { return wl >= 0 ? max(0, i + delta - wl) : 0; };
+    auto lo_of = [&](int i) __attribute__((always_inline)) {
+        return wl >= 0 ? max(0, i + delta - wl) : 0;
+    };
     auto hi_of = [&](int i) __attribute__((always_inline)) {
         int h = sk - 1;
         if (causal) h = min(h, i + delta);
@@ -160,230 +160,90 @@ void fa_fwd_kernel(FwdParams p) {
         return h;
     };
 
+    // ---- tile ranges -------------------------------------------------------
     const int wg_last = min(q0 + T::BM, sq) - 1;
     const int kv_lo = lo_of(q0), kv_hi = hi_of(wg_last);
     const int tile_lo = kv_lo / T::BN;
     const int ntiles = kv_hi >= kv_lo ? kv_hi / T::BN - tile_lo + 1 : 0;
     const int tile_last = tile_lo + ntiles - 1;
 
-    // this wave's rows and key bounds
+    // This wave's rows r0..r1; it computes tiles [pw_lo, pw_hi] and needs no
+    // mask on tiles [in_lo, in_hi] (every row of the wave sees every key).
     const int r0 = q0 + T::WR * wave;
-    const bool wave_active = r0 < sq;
     const int r1 = min(r0 + T::WR - 1, sq - 1);
-    const int w_lo = lo_of(r0), w_hi = wave_active ? hi_of(r1) : -1;
-    const int int_lo = lo_of(r1), int_hi = hi_of(r0);   // keys every row of the wave sees
-    auto part = [&](int jt) __attribute__((always_inline)) {                  // wave has a visible key in tile jt
-        return wave_active && jt * T::BN <= w_hi && jt * T::BN + T::BN - 1 >= w_lo;
+    int pw_lo = 1, pw_hi = 0;
+    if (r0 < sq) {
+        const int wlo = lo_of(r0), whi = hi_of(r1);
+        if (whi >= wlo) { pw_lo = wlo / T::BN; pw_hi = whi / T::BN; }
+    }
+    const int int_lo = lo_of(r1), int_hi = hi_of(r0);
+    const int in_lo = (int_lo + T::BN - 1) / T::BN;
+    const int in_hi = int_hi + 1 >= T::BN ? (int_hi + 1) / T::BN - 1 : -1;
+    auto part = [&](int jt) __attribute__((always_inline)) { return jt >= pw_lo && jt <= pw_hi; };
+    auto interior = [&](int jt) __attribute__((always_inline)) {
+        return jt >= in_lo && jt <= in_hi;
     };
-    auto interior = [&](int jt) __attribute__((always_inline)) {              // every row of the wave sees every key of jt
-        return jt * T::BN >= int_lo && jt * T::BN + T::BN - 1 <= int_hi;
-    };
+    // steps j whose next tile is computed unmasked by this wave: the
+    // straight-line fast path
+    const int fast_lo = max(pw_lo, in_lo - 1);
+    const int fast_hi = min(min(pw_hi - 1, in_hi - 1), tile_last - 1);
 
-    // ---- buffer resources ------------------------------------------------
-    const long long tok_bytes_kv = p.kv_tok_stride * 2;
-    const long long tok_bytes_q = p.q_tok_stride * 2;
-    const char* kseq = (const char*)p.k + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
-    const char* vseq = (const char*)p.v + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
-    // tiles outside [tile_lo, tile_last] get zero records: their loads write
-    // zeros to LDS without touching memory (keeps per-step load counts fixed)
-    auto tile_rsrc = [&](const char* base, int jt) __attribute__((always_inline)) {
-        const bool valid = jt >= tile_lo && jt <= tile_last;
-        const int rows_left = valid ? max(sk - jt * T::BN, 0) : 0;
-        return make_rsrc(base + (long long)jt * T::BN * tok_bytes_kv,
-                         (int)(rows_left * tok_bytes_kv));
-    };
-    // 1 KB LDS blocks of a tile and their per-lane sources.  K block ks, lane
-    // L: key L%32, d-chunk 2*ks + L/32.  V block b, 16-byte unit u = 64*b + L:
-    // blk = u/32 = (2*kk + h)*DB + db, r = u%32 -> key 16*kk + 8*h + 4*(r/16)
-    // + (r/2)%4, d-chunk 4*db + 2*((r/8)%2) + r%2.  The 2*KS blocks of a step
-    // (K blocks, then V blocks) are spread over the waves: wave w issues
-    // blocks w, w + NW, ...
-    int dma_src[T::LPS], dma_soff[T::LPS], dma_dst[T::LPS];
-    bool dma_is_k[T::LPS];
+    // ---- DMA sources -------------------------------------------------------
+    // A step loads TILE_BLOCKS 1 KB blocks of K, then as many of V; wave w
+    // issues blocks w, w + NW, ... of that list.
+    //   K block kb = nb*KS + ks, lane L: key 32*nb + L%32, d-chunk 2*ks + L/32.
+    //   V block vb, 16-byte unit u = 64*vb + L: half-block hb = u/32 =
+    //   kh*DB + db, r = u%32 -> key 8*kh + 4*(r/16) + (r/2)%4, d-chunk
+    //   4*db + 2*((r/8)%2) + r%2.
+    const int tok_bytes_kv = (int)(p.kv_tok_stride * 2);
+    const int tok_bytes_q = (int)(p.q_tok_stride * 2);
+    __builtin_assume(wave >= 0 && wave < T::NW);
+    int dma_voff[T::LPS];
+    uint32_t dma_loff[T::LPS];
+    bool dma_k[T::LPS];
 #pragma unroll
     for (int i = 0; i < T::LPS; ++i) {
         const int gb = wave + i * T::NW;
-        dma_is_k[i] = gb < T::KS;
-        if (dma_is_k[i]) {
-            dma_src[i] = (lane & 31) * (int)tok_bytes_kv + (lane >> 5) * 16;
-            dma_soff[i] = gb * 32;
-            dma_dst[i] = gb * 1024;
+        dma_k[i] = gb < T::TILE_BLOCKS;
+        const int blk = dma_k[i] ? gb : gb - T::TILE_BLOCKS;
+        dma_loff[i] = blk * 1024;
+        if (dma_k[i]) {
+            dma_voff[i] = (32 * (blk / T::KS) + (lane & 31)) * tok_bytes_kv +
+                          (2 * (blk % T::KS) + (lane >> 5)) * 16;
         } else {
-            const int vb = gb - T::KS;
-            const int u = vb * 64 + lane;
-            const int blk = u >> 5, r = u & 31;
-            const int db = blk % T::DB, kh = blk / T::DB;
+            const int hb = 2 * blk + (lane >> 5), r = lane & 31;
+            const int kh = hb / T::DB, db = hb % T::DB;
             const int row = 8 * kh + 4 * (r >> 4) + ((r >> 1) & 3);
             const int chunk = 4 * db + 2 * ((r >> 3) & 1) + (r & 1);
-            dma_src[i] = row * (int)tok_bytes_kv + chunk * 16;
-            dma_soff[i] = 0;
-            dma_dst[i] = vb * 1024;
+            dma_voff[i] = row * tok_bytes_kv + chunk * 16;
         }
     }
-
-    // ---- query blocks as MFMA B operands ---------------------------------
-    u32x4 qreg[T::QB][T::KS];
-    {
-        const auto qrs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const char*)p.q + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2),
-            (short)0, (int)(sq * tok_bytes_q), 0x00020000);   // zero rows past the sequence
-#pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb)
-#pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks) {
-                const int row = r0 + 32 * qb + lq;
-                u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-                    qrs, (int)(row * tok_bytes_q) + (16 * ks + 8 * g) * 2, 0, 0);
-                qreg[qb][ks] = x ^ p.qsign;    // exact negation when scale < 0
-            }
-    }
-
-    f32x16 oacc[T::QB][T::DB];
-#pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[qb][db][e] = 0.f;
-    // running max (log2 units) and this lane's share of the fp32 / 16-bit-rounded sums
-    float m_run[T::QB], l_run[T::QB], lr_run[T::QB];
-#pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) { m_run[qb] = -INFINITY; l_run[qb] = 0.f; lr_run[qb] = 0.f; }
-    const float c = p.c;
-
-    // per-lane visible interval of each query block, relative to its first key 4*g
-    int rel_lo[T::QB], rel_hi[T::QB];
-#pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) {
-        const int pos = r0 + 32 * qb + lq + delta;
-        rel_lo[qb] = (wl >= 0 ? pos - wl : -0x40000000) - 4 * g;
-        int h = sk - 1;
-        if (causal) h = min(h, pos);
-        if (wr >= 0) h = min(h, pos + wr);
-        rel_hi[qb] = h - 4 * g;
-    }
-
-    f32x16 sacc[2][T::QB][T::NB];              // [parity][query block][key block]
-    u32x4 pb[T::QB][T::KK];                    // P as 16-bit B operands
-
-    // ---- phases ----------------------------------------------------------
-    auto qk = [&](f32x16 (&s)[T::QB][T::NB], const uint16_t* kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb)
-#pragma unroll
-            for (int nb = 0; nb < T::NB; ++nb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) s[qb][nb][e] = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < T::NB; ++nb)
-#pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks) {
-                const u32x4 a = *reinterpret_cast<const u32x4*>(kt + ks * 512 + lane * 8);
-#pragma unroll
-                for (int qb = 0; qb < T::QB; ++qb)
-                    s[qb][nb] = mfma32x32x16<BF16>(a, qreg[qb][ks], s[qb][nb]);
-            }
+    const char* kseq = (const char*)p.k + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
+    const char* vseq = (const char*)p.v + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
+    // Tiles outside [tile_lo, tile_last] get zero records: their loads write
+    // zeros to LDS without touching memory (keeps per-step load counts fixed).
+    auto tile_rsrc = [&](const char* base, int jt) __attribute__((always_inline)) {
+        const bool valid = jt >= tile_lo && jt <= tile_last;
+        const int rows = valid ? min(sk - jt * T::BN, T::BN) : 0;
+        return make_rsrc(base + (long long)jt * (T::BN * tok_bytes_kv), rows * tok_bytes_kv);
     };
-    // row max of a tile (masking it first when needed) and the lazy rescale
-    auto rowmax = [&](f32x16 (&s)[T::QB][T::NB], int jt, bool masked) __attribute__((always_inline)) {
-        float mnew[T::QB];
-        bool raise[T::QB];
-        bool any_raise = false;
-#pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb) {
-            if (masked) {
-                const int lo = rel_lo[qb] - jt * T::BN, hi = rel_hi[qb] - jt * T::BN;
-#pragma unroll
-                for (int nb = 0; nb < T::NB; ++nb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int off = 32 * nb + 8 * (e >> 2) + (e & 3);
-                        s[qb][nb][e] = (off >= lo && off <= hi) ? s[qb][nb][e] : -INFINITY;
-                    }
-            }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int nb = 0; nb < T::NB; ++nb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[qb][nb][e]);
-            mx = fmaxf(mx, xor32(mx));
-            mnew[qb] = fmaxf(m_run[qb], mx * c);      // -inf stays -inf (c > 0)
-            raise[qb] = mnew[qb] > m_run[qb] + kRescaleThreshold;
-            any_raise = any_raise || raise[qb];
-        }
-        // Per-row decision (rows are independent); the branch only skips the
-        // work when no row of the wave needs it.  Rows keeping their max are
-        // multiplied by exactly 1.
-        if (wave_any(any_raise)) {
-            asm volatile("");   // keep this rare block a real branch (not speculated)
-#pragma unroll
-            for (int qb = 0; qb < T::QB; ++qb) {
-                const float alpha = raise[qb] ? exp2_fast(m_run[qb] - mnew[qb]) : 1.f;
-                l_run[qb] *= alpha;
-                lr_run[qb] *= alpha;
-#pragma unroll
-                for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[qb][db][e] *= alpha;
-                m_run[qb] = raise[qb] ? mnew[qb] : m_run[qb];
-            }
-        }
+    auto kslot = [&](int jt) __attribute__((always_inline)) {
+        return k_ring + ((jt - tile_lo) & (T::STAGES - 1)) * TE;
     };
-    // P = exp2(S*c - m) as 16-bit B operands; masked scores are -inf -> 0
-    auto softmax_exp = [&](f32x16 (&s)[T::QB][T::NB]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < T::QB; ++qb) {
-            const float m_use = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
-#pragma unroll
-            for (int nb = 0; nb < T::NB; ++nb)
-#pragma unroll
-                for (int e = 0; e < 16; e += 2) {
-                    const float x0 = exp2_fast(fmaf(s[qb][nb][e], c, -m_use));
-                    const float x1 = exp2_fast(fmaf(s[qb][nb][e + 1], c, -m_use));
-                    const uint32_t pk = pack2<BF16>(x0, x1);
-                    // element e of key block nb is slot (e & 7) of reduction step 2*nb + (e >> 3)
-                    pb[qb][2 * nb + (e >> 3)][(e & 7) >> 1] = pk;
-                    // two normalisers: O is divided by the sum of the 16-bit weights
-                    // actually fed to P.V (so its weights sum to one); LSE uses the sum
-                    // of the fp32 values (16-bit rounding would bias it by up to 2^-9)
-                    l_run[qb] += x0 + x1;
-                    lr_run[qb] = dot2_ones<BF16>(pk, lr_run[qb]);
-                }
-        }
+    auto vslot = [&](int jt) __attribute__((always_inline)) {
+        return v_ring + ((jt - tile_lo) & (T::STAGES - 1)) * TE;
     };
-    auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-            for (int kk = 0; kk < T::KK; ++kk) {
-                const uint16_t* base = vt + ((2 * kk) * T::DB + db) * 256 + lane * 4;
-                const u32x2 lo = ds_read_tr16(base);                    // keys 16kk + 4g + 0..3
-                const u32x2 hi = ds_read_tr16(base + T::DB * 256);      // keys 16kk + 8 + 4g + 0..3
-                const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
-#pragma unroll
-                for (int qb = 0; qb < T::QB; ++qb)
-                    oacc[qb][db] = mfma32x32x16<BF16>(a, pb[qb][kk], oacc[qb][db]);
-            }
-    };
-
-    // Ring slot of tile t (t >= tile_lo - 1).
-    auto kslot = [&](int t) __attribute__((always_inline)) {
-        return k_ring + ((t - tile_lo + T::STAGES) % T::STAGES) * TILE_ELEMS;
-    };
-    auto vslot = [&](int t) __attribute__((always_inline)) {
-        return v_ring + ((t - tile_lo + T::STAGES) % T::STAGES) * TILE_ELEMS;
-    };
-    // Load set of step t: K_t and V_{t-1}.  Step j issues set j + STAGES,
+    // Load set of step s: K_s and V_{s-1}.  Step j issues set j + STAGES,
     // which refills the slots of K_j and V_{j-1} (both consumed by step j-1).
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        const i32x4 krs = tile_rsrc(kseq, t), vrs = tile_rsrc(vseq, t - 1);
-        const uint32_t kdst = lds_addr(kslot(t)), vdst = lds_addr(vslot(t - 1));
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const i32x4 krs = tile_rsrc(kseq, s), vrs = tile_rsrc(vseq, s - 1);
+        const uint32_t kdst = lds_addr(kslot(s)), vdst = lds_addr(vslot(s - 1));
 #pragma unroll
         for (int i = 0; i < T::LPS; ++i) {
-            if (dma_is_k[i])
-                dma16_to_lds(krs, kdst + dma_dst[i], dma_src[i], dma_soff[i]);
+            if (dma_k[i])
+                dma16_to_lds(krs, kdst + dma_loff[i], dma_voff[i], 0);
             else
-                dma16_to_lds(vrs, vdst + dma_dst[i], dma_src[i], dma_soff[i]);
+                dma16_to_lds(vrs, vdst + dma_loff[i], dma_voff[i], 0);
         }
     };
     // Before step j the sets up to j+1 (K_{j+1}, V_j) must have landed in
@@ -395,22 +255,140 @@ void fa_fwd_kernel(FwdParams p) {
                      ::"n"(T::LPS * (T::STAGES - 2)) : "memory");
     };
 
+    // ---- the wave's 32 query rows as MFMA B operands ---------------------
+    u32x4 qreg[T::KS];
+    {
+        const auto qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const char*)p.q + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2),
+            (short)0, sq * tok_bytes_q, 0x00020000);   // rows past the sequence read as zeros
+        const int row = r0 + lq;
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) {
+            u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+                qrs, row * tok_bytes_q + (16 * ks + 8 * g) * 2, 0, 0);
+            qreg[ks] = x ^ p.qsign;            // exact negation when scale < 0
+        }
+    }
+
+    f32x16 oacc[T::DB];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+    // running max (log2 units) and this lane's share of the fp32 / 16-bit sums
+    float m_run = -INFINITY, l_run = 0.f, lr_run = 0.f;
+    const float c = p.c;
+
+    // this lane's visible key interval, relative to its first key offset 4*g
+    int rel_lo, rel_hi;
+    {
+        const int pos = r0 + lq + delta;
+        rel_lo = (wl >= 0 ? pos - wl : -0x40000000) - 4 * g;
+        int h = sk - 1;
+        if (causal) h = min(h, pos);
+        if (wr >= 0) h = min(h, pos + wr);
+        rel_hi = h - 4 * g;
+    }
+
+    f32x16 sacc[2][T::NB];                     // [parity][key block]
+    u32x4 pb[T::KK];                           // P as 16-bit B operands
+
+    // ---- phases ----------------------------------------------------------
+    auto qk = [&](f32x16 (&s)[T::NB], const uint16_t* kt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[nb][e] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(
+                    kt + (nb * T::KS + ks) * 512 + lane * 8);
+                s[nb] = mfma32x32x16<BF16>(a, qreg[ks], s[nb]);
+            }
+        }
+    };
+    // row max of a tile (masking it first when needed) and the lazy rescale
+    auto rowmax = [&](f32x16 (&s)[T::NB], int jt, bool masked) __attribute__((always_inline)) {
+        if (masked) {
+            const int lo = rel_lo - jt * T::BN, hi = rel_hi - jt * T::BN;
+#pragma unroll
+            for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int off = 32 * nb + 8 * (e >> 2) + (e & 3);
+                    s[nb][e] = (off >= lo && off <= hi) ? s[nb][e] : -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
+        mx = fmaxf(mx, xor32(mx));
+        const float mnew = fmaxf(m_run, mx * c);       // -inf stays -inf (c > 0)
+        // Per-row decision (rows are independent); the branch only skips the
+        // work when no row of the wave needs it.  Rows keeping their max are
+        // multiplied by exactly 1.
+        const bool raise = mnew > m_run + kRescaleThreshold;
+        if (wave_any(raise)) {
+            asm volatile("");   // keep this rare block a real branch (not speculated)
+            const float alpha = raise ? exp2_fast(m_run - mnew) : 1.f;
+            l_run *= alpha;
+            lr_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            m_run = raise ? mnew : m_run;
+        }
+    };
+    // P = exp2(S*c - m) as 16-bit B operands; masked scores are -inf -> 0
+    auto softmax_exp = [&](f32x16 (&s)[T::NB]) __attribute__((always_inline)) {
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+        for (int nb = 0; nb < T::NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const float x0 = exp2_fast(fmaf(s[nb][e], c, -m_use));
+                const float x1 = exp2_fast(fmaf(s[nb][e + 1], c, -m_use));
+                const uint32_t pk = pack2<BF16>(x0, x1);
+                // element e of key block nb is slot (e & 7) of reduction step 2*nb + (e >> 3)
+                pb[2 * nb + (e >> 3)][(e & 7) >> 1] = pk;
+                // two normalisers: O is divided by the sum of the 16-bit weights
+                // actually fed to P.V (so its weights sum to one); LSE uses the sum
+                // of the fp32 values (16-bit rounding would bias it by up to 2^-9)
+                l_run += x0 + x1;
+                lr_run = dot2_ones<BF16>(pk, lr_run);
+            }
+    };
+    auto pv = [&](const uint16_t* vt) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < T::KK; ++kk)
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db) {
+                const uint16_t* base = vt + ((2 * kk) * T::DB + db) * 256 + lane * 4;
+                const u32x2 lo = ds_read_tr16(base);                    // keys 16kk + 4g + 0..3
+                const u32x2 hi = ds_read_tr16(base + T::DB * 256);      // keys 16kk + 8 + 4g + 0..3
+                const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
+                oacc[db] = mfma32x32x16<BF16>(a, pb[kk], oacc[db]);
+            }
+    };
+
     // One tile step.  On entry tile j's scores (scur) carry their final row
     // max; K_{j+1} and V_j are in the ring.
-    auto step = [&](f32x16 (&scur)[T::QB][T::NB], f32x16 (&snext)[T::QB][T::NB], int j)
+    auto step = [&](f32x16 (&scur)[T::NB], f32x16 (&snext)[T::NB], int j)
         __attribute__((always_inline)) {
         issue(j + T::STAGES);
-        const bool has_next = j + 1 <= tile_last;
-        const bool pj = part(j), pn = has_next && part(j + 1);
-        if (pj && pn && interior(j + 1)) {
+        if (j >= fast_lo && j <= fast_hi) {
             // steady state: one straight-line block
             qk(snext, kslot(j + 1));
             softmax_exp(scur);
             pv(vslot(j));
             rowmax(snext, j + 1, false);
         } else {
+            const bool pn = j + 1 <= tile_last && part(j + 1);
             if (pn) qk(snext, kslot(j + 1));
-            if (pj) {
+            if (part(j)) {
                 softmax_exp(scur);
                 pv(vslot(j));
             }
@@ -420,7 +398,7 @@ void fa_fwd_kernel(FwdParams p) {
     };
 
     if (ntiles > 0) {
-        for (int t = tile_lo; t < tile_lo + T::STAGES; ++t) issue(t);
+        for (int s = tile_lo; s < tile_lo + T::STAGES; ++s) issue(s);
         sync_tile();
         if (part(tile_lo)) {
             qk(sacc[0], kslot(tile_lo));
@@ -438,29 +416,25 @@ void fa_fwd_kernel(FwdParams p) {
     // ---- epilogue: normalise once, write O and LSE -----------------------
     const auto ors = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((char*)p.o + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2), (short)0,
-        (int)(sq * tok_bytes_q), 0x00020000);
+        sq * tok_bytes_q, 0x00020000);          // rows past the sequence are dropped
+    const float l_tot = l_run + xor32(l_run);
+    const float lr_tot = lr_run + xor32(lr_run);
+    const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+    const int row = r0 + lq;
 #pragma unroll
-    for (int qb = 0; qb < T::QB; ++qb) {
-        const float l_tot = l_run[qb] + xor32(l_run[qb]);
-        const float lr_tot = lr_run[qb] + xor32(lr_run[qb]);
-        const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
-        const int row = r0 + 32 * qb + lq;
+    for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                u32x2 w;
-                w.x = pack2<BF16>(oacc[qb][db][4 * jj + 0] * inv, oacc[qb][db][4 * jj + 1] * inv);
-                w.y = pack2<BF16>(oacc[qb][db][4 * jj + 2] * inv, oacc[qb][db][4 * jj + 3] * inv);
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    w, ors, (int)(row * tok_bytes_q) + (32 * db + 8 * jj + 4 * g) * 2, 0, 0);
-            }
-        if (p.lse != nullptr && g == 0 && row < sq) {
-            const long long row_base = VARLEN ? q_tok0 : 0;
-            const float lse = l_tot > 0.f ? (m_run[qb] + log2_fast(l_tot)) * kLn2 : -INFINITY;
-            p.lse[(long long)b * p.lse_b_stride + (long long)hq * p.lse_h_stride + row_base + row] =
-                lse;
+        for (int jj = 0; jj < 4; ++jj) {
+            u32x2 w;
+            w.x = pack2<BF16>(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
+            w.y = pack2<BF16>(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                w, ors, row * tok_bytes_q + (32 * db + 8 * jj + 4 * g) * 2, 0, 0);
         }
+    if (p.lse != nullptr && g == 0 && row < sq) {
+        const long long row_base = VARLEN ? q_tok0 : 0;
+        const float lse = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
+        p.lse[(long long)b * p.lse_b_stride + (long long)hq * p.lse_h_stride + row_base + row] = lse;
     }
 }
 
