@@ -60,9 +60,15 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, uint32_t hi_src
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value held by lane l ^ 32 (the other half of a 64-wide wave).
+// Value held by lane l ^ 32 (the other half of a 64-wide wave), via the
+// gfx950 v_permlane32_swap (a VALU lane swap, no LDS round trip).  Swapping
+// x with itself leaves lanes 0-31 of the first result and lanes 32-63 of the
+// second result unchanged; the other halves receive the partner's value.
 __device__ __forceinline__ float xor32(float x) {
-    return __shfl_xor(x, 32, 64);
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const bool lower = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 32) == 0;
+    return __builtin_bit_cast(float, lower ? r[1] : r[0]);
 }
 
 __device__ __forceinline__ bool wave_any(bool p) {

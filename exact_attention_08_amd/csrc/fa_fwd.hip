@@ -319,11 +319,19 @@ void fa_fwd_kernel(FwdParams p) {
                     s[nb][e] = (off >= lo && off <= hi) ? s[nb][e] : -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        // tree reduction (short dependency chain)
+        float m4[4 * T::NB];
 #pragma unroll
         for (int nb = 0; nb < T::NB; ++nb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
+            for (int q4 = 0; q4 < 4; ++q4)
+                m4[4 * nb + q4] = fmaxf(fmaxf(s[nb][4 * q4], s[nb][4 * q4 + 1]),
+                                        fmaxf(s[nb][4 * q4 + 2], s[nb][4 * q4 + 3]));
+#pragma unroll
+        for (int w = 4 * T::NB; w > 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w / 2; ++i) m4[i] = fmaxf(m4[i], m4[i + w / 2]);
+        float mx = m4[0];
         mx = fmaxf(mx, xor32(mx));
         const float mnew = fmaxf(m_run, mx * c);       // -inf stays -inf (c > 0)
         // Per-row decision (rows are independent); the branch only skips the
