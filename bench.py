@@ -13,8 +13,10 @@ runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +29,42 @@ if ROOT not in sys.path:
 from exact_attention_08_amd import fa, metrics, synth  # noqa: E402
 
 METRIC = "attn fwd TFLOP/s (causal-adj) & % bf16 MFMA peak; decode HBM GB/s"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_08_amd", "csrc")
+COPY_BYTES = 1 << 30          # plain-copy calibration: 1 GiB read + 1 GiB written
+
+
+def source_hash(name: str) -> str:
+    """sha256 of a kernel source file (ties profiled counters to the code)."""
+    with open(os.path.join(KERNEL_SRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def profiled_traffic(summary: str, src: str):
+    """HBM bytes per launch recorded in a committed rocprofv3 summary, or None
+    when the summary is missing or the kernel source changed since."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"source_sha256:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not h or not t or h.group(1) != source_hash(src):
+        return None
+    return int(t.group(1))
+
+
+def copy_calibration():
+    """A plain device copy of known size, run under rocprofv3 --pmc to scale
+    FETCH_SIZE / WRITE_SIZE to bytes."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES,
+                      "copies": 3}), flush=True)
 
 
 def _timed(fn, steps: int, warmup: int):
@@ -126,6 +164,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this attention build runs on exactly one GPU; --gpus must be 1",
@@ -134,6 +174,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     fa.load()   # fails loudly if the HIP library is not built
 
     w = synth.WORKLOADS[args.workload]
@@ -160,7 +203,8 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "fa_fwd_kernel<128,bf16>",
                      "achieved": round(tflops_ev, 2), "peak": metrics.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops_ev / metrics.PEAK_BF16_TFLOPS, 4),
-                     "avg_launch_ms": round(ev, 5), "traffic": None},
+                     "avg_launch_ms": round(ev, 5),
+                     "traffic": profiled_traffic(f"fa_fwd_kernel_{w.name}.md", "fa_fwd.hip")},
     }
     if not args.no_decode:
         del q
