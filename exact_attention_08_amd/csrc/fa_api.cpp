@@ -188,7 +188,7 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
     p.max_len = max_seqlen_k;
     p.split = split_size;
     p.nsplit = (max_seqlen_k + split_size - 1) / split_size;
-    p.qblocks = (p.G + 31) / 32;
+    p.qblocks = (p.G + 15) / 16;
     p.ws_o = static_cast<float*>(workspace);
     p.ws_lse = p.ws_o + (size_t)B * Hq * p.nsplit * d;
     p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;

@@ -5,19 +5,22 @@
 // "Long context beyond a single GPU" (partials merged with the same online
 // softmax rule).
 //
-// Split kernel: one wave per (split, query block, K/V head, sequence).  The
-// wave owns all G = Hq/Hkv query heads that read its K/V head (up to 32 per
-// query block), so every cache byte is read exactly once.  Keys are walked
-// in blocks of 32; the next block's loads are issued before the current
-// block is computed.  The path is HBM-bound (4 FLOP per cache byte at G=4),
-// so the MFMA tile is mostly padding and that is fine: S^T = K Q^T and
-// O^T = V^T P^T run on v_mfma_f32_32x32x16 with K and V loaded straight from
-// HBM into operand registers (no LDS):
-//   * K operand: lane (key l%32, half g) reads d-range [g*d/2, (g+1)*d/2)
-//     of its key row, one contiguous d-byte run; Q uses the same d order.
-//   * V operand: output row m of accumulator db is column m*DB + db, so a
-//     lane needs DB adjacent columns of each of its 16 keys: one 2*DB-byte
-//     load per key, then 16-bit halves are regrouped in registers.
+// Split kernel: one wave per (split, query block of up to 16 query heads,
+// K/V head, sequence).  The wave owns all query heads that read its K/V head
+// (G = Hq/Hkv, up to 16 per query block), so every cache byte is read exactly
+// once.  Keys are walked in blocks of 32; the next block's loads are issued
+// before the current block is computed.  The path is HBM-bound (4 FLOP per
+// cache byte at G=4), so the MFMA tile is mostly padding and that is fine:
+// S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32 (16 query
+// columns: little register space is spent on padding) with K and V loaded
+// straight from HBM into operand registers (no LDS):
+//   * K operand: lane (key l%16, quarter q = l/16) reads d-range
+//     [q*d/4, (q+1)*d/4) of its key row, one contiguous run; Q uses the same
+//     d order.
+//   * V operand: accumulator db row m is column m*(d/16) + db, so a lane
+//     needs d/16 adjacent columns of each of its 8 keys: one 16-byte (d=128)
+//     load per key, 16 lanes covering a whole 256-byte row; 16-bit halves are
+//     regrouped in registers.
 // Each split writes a normalised fp32 partial O_c and its LSE_c.
 //
 // Combine kernel: one wave per (sequence, query head); with M = max_c LSE_c,
@@ -31,11 +34,13 @@ namespace fa {
 constexpr float kDecodeRescaleThreshold = 8.0f;   // log2 units, as in the forward kernel
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
-    constexpr int KS = D / 16;          // reduction steps over d
-    constexpr int DB = D / 32;          // O^T accumulators
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void fa_decode_split_kernel(DecodeParams p) {
+    constexpr int KS = D / 32;          // reduction steps over d (16x16x32)
+    constexpr int DQ = D / 4;           // d-range per lane quarter
+    constexpr int DB = D / 16;          // O^T accumulators (16 columns each)
     const int lane = threadIdx.x;
-    const int lq = lane & 31, g = lane >> 5;
+    const int lq = lane & 15, q4 = lane >> 4;
 
     int i = blockIdx.x;
     const int split_idx = i % p.nsplit; i /= p.nsplit;
@@ -53,7 +58,7 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
     const int ka = max(split_idx * p.split, lo);
     const int kb = min((split_idx + 1) * p.split, L);
 
-    const int qh_local = 32 * qb + lq;          // query head within the group
+    const int qh_local = 16 * qb + lq;          // query head within the group
     const bool q_valid = qh_local < p.G;
     const int hq = hkv * p.G + qh_local;
 
@@ -65,7 +70,7 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
 
     u32x4 qreg[KS];
     {
-        const uint16_t* qrow = (const uint16_t*)p.q + ((long long)b * p.Hq + hq) * D + g * (D / 2);
+        const uint16_t* qrow = (const uint16_t*)p.q + ((long long)b * p.Hq + hq) * D + q4 * DQ;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 x = q_valid ? ld_global16(qrow + ks * 8) : (u32x4){0u, 0u, 0u, 0u};
@@ -73,108 +78,114 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
         }
     }
 
-    // key (within a 32-key block) of reduction slot sl of step kk for half g
-    auto slot_key = [&](int kk, int sl) __attribute__((always_inline)) {
-        return 16 * kk + (sl < 4 ? 4 * g + sl : 8 + 4 * g + (sl - 4));
+    // key (within a 32-key block) of P.V reduction slot sl for this quarter
+    auto slot_key = [&](int sl) __attribute__((always_inline)) {
+        return sl < 4 ? 4 * q4 + sl : 16 + 4 * q4 + (sl - 4);
     };
 
     typedef uint32_t vec_t __attribute__((ext_vector_type(DB / 2)));
     struct Block {
-        u32x4 k[KS];
-        vec_t v[16];
+        u32x4 k[2][KS];                 // two 16-key halves
+        vec_t v[8];                     // this lane's 8 keys x DB columns
     };
     auto load_block = [&](Block& blk, int jb) __attribute__((always_inline)) {
-        const int jk = jb + lq;
-        const bool kin = jk >= ka && jk < kb;
-        const uint16_t* krow = kseq + (long long)jk * tok_stride + g * (D / 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            blk.k[ks] = kin ? ld_global16(krow + ks * 8) : (u32x4){0u, 0u, 0u, 0u};
+        for (int h = 0; h < 2; ++h) {
+            const int jk = jb + 16 * h + lq;
+            const bool kin = jk >= ka && jk < kb;
+            const uint16_t* krow = kseq + (long long)jk * tok_stride + q4 * DQ;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            for (int ks = 0; ks < KS; ++ks)
+                blk.k[h][ks] = kin ? ld_global16(krow + ks * 8) : (u32x4){0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int sl = 0; sl < 8; ++sl) {
-                const int j = jb + slot_key(kk, sl);
-                const bool vin = j >= ka && j < kb;
-                vec_t x;
-                for (int w = 0; w < DB / 2; ++w) x[w] = 0u;
-                if (vin) x = *reinterpret_cast<const vec_t*>(vseq + (long long)j * tok_stride + lq * DB);
-                blk.v[8 * kk + sl] = x;
-            }
+        for (int sl = 0; sl < 8; ++sl) {
+            const int j = jb + slot_key(sl);
+            const bool vin = j >= ka && j < kb;
+            vec_t x;
+#pragma unroll
+            for (int w = 0; w < DB / 2; ++w) x[w] = 0u;
+            if (vin) x = *reinterpret_cast<const vec_t*>(vseq + (long long)j * tok_stride + lq * DB);
+            blk.v[sl] = x;
+        }
     };
 
-    f32x16 oacc[DB];
+    f32x4 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oacc[db][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f, lr_run = 0.f;
     const float c = p.c;
 
     auto process = [&](const Block& cur, int jb) __attribute__((always_inline)) {
-        f32x16 s;
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
+        f32x4 s[2];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16<BF16>(cur.k[ks], qreg[ks], s);
-
-        // element e: key jb + 8*(e>>2) + 4*g + (e&3); visible iff ka <= key < kb
-        const int rlo = ka - jb - 4 * g, rhi = kb - 1 - jb - 4 * g;
-        const bool edge = jb < ka || jb + 31 >= kb;
-        float mx = -INFINITY;
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int off = 8 * (e >> 2) + (e & 3);
-            const bool vis = !edge || (off >= rlo && off <= rhi);
-            mx = fmaxf(mx, vis ? s[e] : -INFINITY);
+            for (int e = 0; e < 4; ++e) s[h][e] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) s[h] = mfma16x16x32<BF16>(cur.k[h][ks], qreg[ks], s[h]);
         }
+        // element e of half h: key jb + 16*h + 4*q4 + e; visible iff ka <= key < kb
+        const int rlo = ka - jb - 4 * q4, rhi = kb - 1 - jb - 4 * q4;
+        const bool edge = jb < ka || jb + 31 >= kb;
+        if (edge) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int off = 16 * h + e;
+                    s[h][e] = (off >= rlo && off <= rhi) ? s[h][e] : -INFINITY;
+                }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, xor32(mx));
-        const float m_tile = mx == -INFINITY ? -INFINITY : mx * c;
-        const float m_new = fmaxf(m_run, m_tile);
-        // Per-row decision (rows are independent); the branch only skips
-        // the work when no row of the wave needs it.  Rows that keep their
-        // max are multiplied by exactly 1.
+        const float m_new = fmaxf(m_run, mx * c);
+        // Per-row decision (rows are independent); rows keeping their max are
+        // multiplied by exactly 1.
         const bool raise = m_new > m_run + kDecodeRescaleThreshold;
         if (wave_any(raise)) {
             asm volatile("");   // keep this rare block a real branch (not speculated)
             const float alpha = raise ? exp2_fast(m_run - m_new) : 1.f;
             l_run *= alpha;
+            lr_run *= alpha;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[db][e] *= alpha;
             m_run = raise ? m_new : m_run;
         }
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
 
-        u32x4 pb[2];
+        // P^T as the B operand: slots 0-3 are half 0, slots 4-7 half 1
+        u32x4 pb;
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-            float pv[2];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int ee = e + u;
-                const int off = 8 * (ee >> 2) + (ee & 3);
-                const bool vis = !edge || (off >= rlo && off <= rhi);
-                const float x = exp2_fast(fmaf(s[ee], c, -m_use));
-                pv[u] = vis ? x : 0.f;
-                l_run += pv[u];
+            for (int e = 0; e < 4; e += 2) {
+                const float x0 = exp2_fast(fmaf(s[h][e], c, -m_use));
+                const float x1 = exp2_fast(fmaf(s[h][e + 1], c, -m_use));
+                const uint32_t pk = pack2<BF16>(x0, x1);
+                pb[2 * h + (e >> 1)] = pk;
+                l_run += x0 + x1;
+                lr_run = dot2_ones<BF16>(pk, lr_run);
             }
-            pb[e >> 3][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
-        }
 
         // O^T += V^T P^T ; accumulator db row m is column m*DB + db
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db) {
+            u32x4 a;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                u32x4 a;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t x0 = cur.v[8 * kk + 2 * w][db >> 1];
-                    const uint32_t x1 = cur.v[8 * kk + 2 * w + 1][db >> 1];
-                    a[w] = (db & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u))
-                                    : ((x0 & 0xffffu) | (x1 << 16));
-                }
-                oacc[db] = mfma32x32x16<BF16>(a, pb[kk], oacc[db]);
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x0 = cur.v[2 * w][db >> 1];
+                const uint32_t x1 = cur.v[2 * w + 1][db >> 1];
+                a[w] = (db & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
             }
+            oacc[db] = mfma16x16x32<BF16>(a, pb, oacc[db]);
+        }
     };
 
     // two register sets: the next block's loads are in flight while the
@@ -190,27 +201,26 @@ __global__ __launch_bounds__(64) void fa_decode_split_kernel(DecodeParams p) {
         process(b1, jb + 32);
     }
 
-    // normalised partial of this split
-    const float l_tot = l_run + xor32(l_run);
+    // normalised partial of this split (O by the sum of the 16-bit weights,
+    // LSE by the fp32 sum, as in the forward kernel)
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += xor32(l_tot);
+    float lr_tot = lr_run + __shfl_xor(lr_run, 16, 64);
+    lr_tot += xor32(lr_tot);
     if (q_valid) {
         const long long row = ((long long)b * p.Hq + hq) * p.nsplit + split_idx;
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
         float* orow = p.ws_o + row * D;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int k = 0; k < 4; ++k) {
+            const int m = 4 * q4 + k;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int m = 8 * jj + 4 * g + k;
-                float vals[DB];
-#pragma unroll
-                for (int db = 0; db < DB; ++db) vals[db] = oacc[db][4 * jj + k] * inv;
-                if constexpr (DB == 4) {
-                    *reinterpret_cast<f32x4*>(orow + m * DB) = (f32x4){vals[0], vals[1], vals[2], vals[3]};
-                } else {
-                    *reinterpret_cast<f32x2*>(orow + m * DB) = (f32x2){vals[0], vals[1]};
-                }
-            }
-        if (g == 0)
+            for (int d4 = 0; d4 < DB; d4 += 4)
+                *reinterpret_cast<f32x4*>(orow + m * DB + d4) =
+                    (f32x4){oacc[d4][k] * inv, oacc[d4 + 1][k] * inv, oacc[d4 + 2][k] * inv,
+                            oacc[d4 + 3][k] * inv};
+        }
+        if (q4 == 0)
             p.ws_lse[row] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
     }
 }

@@ -25,6 +25,20 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Operand registers: lane l holds row (A) / column (B) l%32 and the 8
 // reduction slots of half l/32.  Result: lane l holds column l%32, element
 // 4*jj+k of the accumulator is row 8*jj + 4*(l/32) + k.
+// One v_mfma_f32_16x16x32_{bf16,f16}: C[16x16] += A[16x32] * B[32x16].
+// Lane l holds row (A) / column (B) l%16 and the 8 reduction slots of
+// quarter l/16; result lane l holds column l%16, rows 4*(l/16) + 0..3.
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+}
+
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     if constexpr (BF16) {
@@ -55,6 +69,18 @@ template <bool SEL_HI>
 __device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, uint32_t hi_src) {
     // v_perm_b32: byte selector over {hi_src (bytes 4-7), lo_src (bytes 0-3)}
     return __builtin_amdgcn_perm(hi_src, lo_src, SEL_HI ? 0x07060302u : 0x05040100u);
+}
+
+// acc + lo + hi of a dword holding two 16-bit values (v_dot2 against (1, 1)).
+template <bool BF16>
+__device__ __forceinline__ float dot2_ones(uint32_t packed, float acc) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
+                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed),
+                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+    }
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -83,17 +83,6 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
-template <bool BF16>
-__device__ __forceinline__ float dot2_ones(uint32_t packed, float acc) {
-    if constexpr (BF16) {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
-                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
-    } else {
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed),
-                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
-    }
-}
-
 template <int D, bool BF16, bool VARLEN>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdParams p) {

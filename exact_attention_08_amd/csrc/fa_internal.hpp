@@ -43,7 +43,7 @@ struct DecodeParams {
     int Sk_cap;
     int max_len;                // host bound on cache lengths (lengths are clamped to it)
     int nsplit, split;
-    int qblocks;                // ceil(G / 32)
+    int qblocks;                // ceil(G / 16)
     int causal, wl, wr;
     float c;                    // |scale| * log2(e)
     uint32_t qsign;
