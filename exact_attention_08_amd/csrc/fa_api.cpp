@@ -111,7 +111,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
     set_scale(softmax_scale, &p.c, &p.qsign);
     p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
-    if ((long long)p.nqt * Hq * B * 256 > kMaxGridThreads)
+    if ((long long)p.nqt * Hq * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
     return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
 }
@@ -146,7 +146,7 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out
     p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
     set_scale(softmax_scale, &p.c, &p.qsign);
     p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
-    if ((long long)p.nqt * Hq * B * 256 > kMaxGridThreads)
+    if ((long long)p.nqt * Hq * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
     return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, true, stream));
 }
@@ -193,7 +193,7 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
     p.ws_lse = p.ws_o + (size_t)B * Hq * p.nsplit * d;
     p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
     set_scale(softmax_scale, &p.c, &p.qsign);
-    if ((long long)p.nsplit * p.qblocks * Hkv * B * 64 > kMaxGridThreads)
+    if ((long long)p.nsplit * p.qblocks * Hkv * B * fa::kDecodeThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
     return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
 }

@@ -5,27 +5,32 @@
 // "Long context beyond a single GPU" (partials merged with the same online
 // softmax rule).
 //
-// Split kernel: one wave per (split, query block of up to 16 query heads,
-// K/V head, sequence).  The wave owns all query heads that read its K/V head
-// (G = Hq/Hkv, up to 16 per query block), so every cache byte is read exactly
-// once.  Keys are walked in blocks of 32; the next block's loads are issued
-// before the current block is computed.  The path is HBM-bound (4 FLOP per
-// cache byte at G=4), so the MFMA tile is mostly padding and that is fine:
-// S^T = K Q^T and O^T = V^T P^T run on v_mfma_f32_16x16x32 (16 query
-// columns: little register space is spent on padding) with K and V loaded
-// straight from HBM into operand registers (no LDS):
-//   * K operand: lane (key l%16, quarter q = l/16) reads d-range
-//     [q*d/4, (q+1)*d/4) of its key row, one contiguous run; Q uses the same
-//     d order.
-//   * V operand: accumulator db row m is column m*(d/16) + db, so a lane
-//     needs d/16 adjacent columns of each of its 8 keys: one 16-byte (d=128)
-//     load per key, 16 lanes covering a whole 256-byte row; 16-bit halves are
-//     regrouped in registers.
+// Split kernel: one work-group of four waves per (split, query block of up
+// to 16 query heads, K/V head, sequence).  The work-group owns all query
+// heads that read its K/V head (G = Hq/Hkv, up to 16 per query block), so
+// every cache byte is read exactly once; its waves take interleaved 32-key
+// blocks of the split and merge their (m, l, O) partials through LDS at the
+// end.  The Hkv heads of one split are adjacent in launch order, so the
+// 2 KiB token rows they share stream from HBM at about the same time.  The
+// path is HBM-bound (4 FLOP per cache byte at G=4): the MFMA tile is mostly
+// padding and that is fine.  S^T = K Q^T and O^T = V^T P^T run on
+// v_mfma_f32_16x16x32 (16 query columns):
+//   * K: copied HBM -> LDS by buffer_load ... lds, each 1 KiB instruction
+//     moving whole rows (whole 128-byte lines; an operand-order register
+//     load would touch only 64 bytes per row per instruction, measurably
+//     slower).  Rows are XOR-swizzled in 16-byte chunks so the operand
+//     reads (lane = key l%16, quarter l/16 = d-chunk 4*ks + l/16) hit all
+//     banks once.  Two slots per wave; block t+2 is copied while t+1 is in
+//     flight.
+//   * V: straight into operand registers: accumulator db row m is column
+//     m*(d/16) + db, so a lane needs d/16 adjacent columns of each of its 8
+//     keys, one 16-byte (d=128) load per key and 16 lanes covering a whole
+//     row; 16-bit halves are regrouped in registers.
 // Each split writes a normalised fp32 partial O_c and its LSE_c.
 //
 // Combine kernel: one wave per (sequence, query head); with M = max_c LSE_c,
 // w_c = exp(LSE_c - M): LSE = M + ln(sum w_c), O = sum w_c O_c / sum w_c,
-// summed in split order (deterministic).
+// summed in split order (deterministic), several partial rows in flight.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -34,23 +39,35 @@ namespace fa {
 constexpr float kDecodeRescaleThreshold = 8.0f;   // log2 units, as in the forward kernel
 
 template <int D, bool BF16>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_decode_split_kernel(DecodeParams p) {
-    constexpr int KS = D / 32;          // reduction steps over d (16x16x32)
-    constexpr int DQ = D / 4;           // d-range per lane quarter
-    constexpr int DB = D / 16;          // O^T accumulators (16 columns each)
-    const int lane = threadIdx.x;
+    constexpr int KS = D / 32;            // reduction steps over d (16x16x32)
+    constexpr int DB = D / 16;            // O^T accumulators (16 columns each)
+    constexpr int NW = kDecodeWaves;
+    constexpr int ROWB = 2 * D;           // bytes of one head's key row
+    constexpr int CH = D / 8;             // 16-byte chunks per row
+    constexpr int RPI = 1024 / ROWB;      // rows per 1 KiB DMA instruction
+    constexpr int SLOT = 32 * ROWB;       // one 32-key K block in LDS
+    constexpr int NKI = SLOT / 1024;      // DMA instructions per K block
+    constexpr int NVI = 8;                // V loads per block (one per key slot)
+    constexpr int RING = NW * 2 * SLOT;   // two K slots per wave
+    constexpr int RED = NW * 16 * (D + 4) * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[RING > RED ? RING : RED];
+    __shared__ float red_s[NW][3][16];    // per-wave m, l (fp32), l (16-bit weights)
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int lq = lane & 15, q4 = lane >> 4;
 
+    // the Hkv heads of one chunk are adjacent in launch order, so the whole
+    // token rows they share are streamed at about the same time
     int i = blockIdx.x;
-    const int split_idx = i % p.nsplit; i /= p.nsplit;
+    const int hkv = i % p.Hkv; i /= p.Hkv;
     const int qb = i % p.qblocks; i /= p.qblocks;
-    const int hkv = i % p.Hkv;
-    const int b = i / p.Hkv;
-
+    const int split_idx = i % p.nsplit;
+    const int b = i / p.nsplit;
     const int L = min(max(p.seqlens[b], 0), p.max_len);
-    const int nsplit_b = (L + p.split - 1) / p.split;
-    if (split_idx >= nsplit_b) return;
+    if (split_idx >= (L + p.split - 1) / p.split) return;   // uniform over the work-group
 
     // The query sits at key position L-1: causal and the right window never
     // hide a cached key; the left window hides keys before L-1-wl.
@@ -62,51 +79,73 @@ void fa_decode_split_kernel(DecodeParams p) {
     const bool q_valid = qh_local < p.G;
     const int hq = hkv * p.G + qh_local;
 
-    const long long tok_stride = (long long)p.Hkv * D;
-    const uint16_t* kseq = (const uint16_t*)p.k + (long long)b * p.Sk_cap * tok_stride +
-                           (long long)hkv * D;
-    const uint16_t* vseq = (const uint16_t*)p.v + (long long)b * p.Sk_cap * tok_stride +
-                           (long long)hkv * D;
+    const int tok_bytes = p.Hkv * ROWB;
+    const long long seq_bytes = (long long)b * p.Sk_cap * tok_bytes;
 
+    // d order of the Q.K reduction: step ks, quarter q4 covers d-chunk
+    // 4*ks + q4 (8 values); Q and K use the same order.
     u32x4 qreg[KS];
     {
-        const uint16_t* qrow = (const uint16_t*)p.q + ((long long)b * p.Hq + hq) * D + q4 * DQ;
+        // rows of padding heads read as zeros
+        const auto qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const uint16_t*)p.q + ((long long)b * p.Hq + hkv * p.G + 16 * qb) * D),
+            (short)0, min(16, p.G - 16 * qb) * ROWB, 0x00020000);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 x = q_valid ? ld_global16(qrow + ks * 8) : (u32x4){0u, 0u, 0u, 0u};
+            const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(qrs, lq * ROWB + (4 * ks + q4) * 16, 0, 0);
             qreg[ks] = x ^ p.qsign;
         }
     }
+
+    // Buffer resource over keys [jb, kb) of this sequence (all heads); rows
+    // at or past kb read as zeros, so no load leaves the cache (a block past
+    // kb reads nothing at all).
+    auto block_rows = [&](int jb) __attribute__((always_inline)) {
+        return max(kb - jb, 0) * tok_bytes;
+    };
+    auto block_rsrc = [&](const void* base, int jb) __attribute__((always_inline)) {
+        return make_rsrc((const char*)base + seq_bytes + (long long)jb * tok_bytes, block_rows(jb));
+    };
+    // K rows in LDS: 16-byte chunk c of row r sits at chunk slot c ^ swz(r),
+    // so the 16 rows one MFMA operand read touches hit 16 distinct bank
+    // groups.
+    auto swz = [](int r) __attribute__((always_inline)) {
+        return (r / (256 / ROWB)) & (CH - 1);
+    };
+    const uint32_t ring = lds_addr(lds) + wave * 2 * SLOT;
+    // K block at key jb into this wave's slot s: each 1 KiB instruction
+    // copies RPI whole rows (whole 128-byte lines from HBM).
+    auto dma_k = [&](int jb, int s) __attribute__((always_inline)) {
+        const i32x4 rs = block_rsrc(p.k, jb);
+#pragma unroll
+        for (int t = 0; t < NKI; ++t) {
+            const int r = t * RPI + lane / CH;
+            const int c = (lane % CH) ^ swz(r);
+            dma16_to_lds(rs, ring + s * SLOT + t * 1024, r * tok_bytes + hkv * ROWB + c * 16, 0);
+        }
+    };
 
     // key (within a 32-key block) of P.V reduction slot sl for this quarter
     auto slot_key = [&](int sl) __attribute__((always_inline)) {
         return sl < 4 ? 4 * q4 + sl : 16 + 4 * q4 + (sl - 4);
     };
-
     typedef uint32_t vec_t __attribute__((ext_vector_type(DB / 2)));
-    struct Block {
-        u32x4 k[2][KS];                 // two 16-key halves
-        vec_t v[8];                     // this lane's 8 keys x DB columns
-    };
-    auto load_block = [&](Block& blk, int jb) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int jk = jb + 16 * h + lq;
-            const bool kin = jk >= ka && jk < kb;
-            const uint16_t* krow = kseq + (long long)jk * tok_stride + q4 * DQ;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                blk.k[h][ks] = kin ? ld_global16(krow + ks * 8) : (u32x4){0u, 0u, 0u, 0u};
-        }
+    struct VBlock { vec_t v[8]; };      // this lane's 8 keys x DB columns
+    // V straight into operand registers: lane lq reads DB adjacent columns,
+    // 16 lanes a whole row.  Keys before ka read as zeros (offset past the
+    // resource), keys at or past kb through the resource bound.
+    auto load_v = [&](VBlock& blk, int jb) __attribute__((always_inline)) {
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const char*)p.v + seq_bytes + (long long)jb * tok_bytes), (short)0,
+            block_rows(jb), 0x00020000);
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
-            const int j = jb + slot_key(sl);
-            const bool vin = j >= ka && j < kb;
-            vec_t x;
-#pragma unroll
-            for (int w = 0; w < DB / 2; ++w) x[w] = 0u;
-            if (vin) x = *reinterpret_cast<const vec_t*>(vseq + (long long)j * tok_stride + lq * DB);
-            blk.v[sl] = x;
+            const int r = slot_key(sl);
+            const int off = jb + r < ka ? 0x7ffffff0 : r * tok_bytes + hkv * ROWB + lq * DB * 2;
+            if constexpr (DB == 8)
+                blk.v[sl] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+            else
+                blk.v[sl] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
         }
     };
 
@@ -118,14 +157,20 @@ void fa_decode_split_kernel(DecodeParams p) {
     float m_run = -INFINITY, l_run = 0.f, lr_run = 0.f;
     const float c = p.c;
 
-    auto process = [&](const Block& cur, int jb) __attribute__((always_inline)) {
-        f32x4 s[2];
+    auto process = [&](int s, const VBlock& vb, int jb) __attribute__((always_inline)) {
+        const unsigned char* kbase = lds + (wave * 2 + s) * SLOT;
+        f32x4 sc[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            const int r = 16 * h + lq;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[h][e] = 0.f;
+            for (int e = 0; e < 4; ++e) sc[h][e] = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) s[h] = mfma16x16x32<BF16>(cur.k[h][ks], qreg[ks], s[h]);
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 kr = *reinterpret_cast<const u32x4*>(
+                    kbase + r * ROWB + (((4 * ks + q4) ^ swz(r)) * 16));
+                sc[h] = mfma16x16x32<BF16>(kr, qreg[ks], sc[h]);
+            }
         }
         // element e of half h: key jb + 16*h + 4*q4 + e; visible iff ka <= key < kb
         const int rlo = ka - jb - 4 * q4, rhi = kb - 1 - jb - 4 * q4;
@@ -136,11 +181,11 @@ void fa_decode_split_kernel(DecodeParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int off = 16 * h + e;
-                    s[h][e] = (off >= rlo && off <= rhi) ? s[h][e] : -INFINITY;
+                    sc[h][e] = (off >= rlo && off <= rhi) ? sc[h][e] : -INFINITY;
                 }
         }
-        float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                         fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, xor32(mx));
         const float m_new = fmaxf(m_run, mx * c);
@@ -166,8 +211,8 @@ void fa_decode_split_kernel(DecodeParams p) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; e += 2) {
-                const float x0 = exp2_fast(fmaf(s[h][e], c, -m_use));
-                const float x1 = exp2_fast(fmaf(s[h][e + 1], c, -m_use));
+                const float x0 = exp2_fast(fmaf(sc[h][e], c, -m_use));
+                const float x1 = exp2_fast(fmaf(sc[h][e + 1], c, -m_use));
                 const uint32_t pk = pack2<BF16>(x0, x1);
                 pb[2 * h + (e >> 1)] = pk;
                 l_run += x0 + x1;
@@ -180,54 +225,107 @@ void fa_decode_split_kernel(DecodeParams p) {
             u32x4 a;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const uint32_t x0 = cur.v[2 * w][db >> 1];
-                const uint32_t x1 = cur.v[2 * w + 1][db >> 1];
+                const uint32_t x0 = vb.v[2 * w][db >> 1];
+                const uint32_t x1 = vb.v[2 * w + 1][db >> 1];
                 a[w] = (db & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
             }
             oacc[db] = mfma16x16x32<BF16>(a, pb, oacc[db]);
         }
     };
 
-    // two register sets: the next block's loads are in flight while the
-    // current block is computed
-    const int jfirst = (ka / 32) * 32;
-    Block b0, b1;
-    if (jfirst < kb) load_block(b0, jfirst);
-    for (int jb = jfirst; jb < kb; jb += 64) {
-        if (jb + 32 < kb) load_block(b1, jb + 32);
-        process(b0, jb);
-        if (jb + 32 >= kb) break;
-        if (jb + 64 < kb) load_block(b0, jb + 64);
-        process(b1, jb + 32);
+    // This wave's blocks are jfirst + STEP*t, t < nb.  K of block t goes to
+    // slot t%2 two blocks ahead; V of block t+1 is loaded while block t is
+    // computed.  Issue order: K0 K1 V0 | V1 K2 | V2 K3 | ...  Every
+    // iteration issues its V loads (past the last block they read nothing),
+    // so the count of loads issued after block t's K is known: V(t), V(t+1)
+    // and, while t+1 < nb, K(t+1).  The explicit vmcnt waits count them; the
+    // compiler tracks the V loads but not the K copies, so its own waits for
+    // V only ever wait for more.
+    const int jfirst = (ka / 32) * 32 + 32 * wave;
+    constexpr int STEP = 32 * NW;
+    const int nb = jfirst < kb ? (kb - 1 - jfirst) / STEP + 1 : 0;
+    VBlock va, vb;
+    if (nb > 0) dma_k(jfirst, 0);
+    if (nb > 1) dma_k(jfirst + STEP, 1);
+    load_v(va, jfirst);
+    auto iter = [&](int t, VBlock& cur, VBlock& next) __attribute__((always_inline)) {
+        const int jb = jfirst + t * STEP;
+        const int s = t & 1;
+        load_v(next, jb + STEP);
+        if (t + 1 < nb)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NVI + NKI) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NVI) : "memory");
+        process(s, cur, jb);
+        if (t + 2 < nb) {
+            // the slot's K reads were consumed by the MFMAs above
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            dma_k(jb + 2 * STEP, s);
+        }
+    };
+    // (no exit in the middle of the unrolled pair: the compiler's view of
+    // which V loads are pending stays exact at the loop head)
+    for (int t = 0; t + 1 < nb; t += 2) {
+        iter(t, va, vb);
+        iter(t + 1, vb, va);
     }
+    if (nb & 1) iter(nb - 1, va, vb);
 
-    // normalised partial of this split (O by the sum of the 16-bit weights,
-    // LSE by the fp32 sum, as in the forward kernel)
+    // ---- merge the waves' partials (same rule as the combine kernel) ------
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += xor32(l_tot);
     float lr_tot = lr_run + __shfl_xor(lr_run, 16, 64);
     lr_tot += xor32(lr_tot);
-    if (q_valid) {
-        const long long row = ((long long)b * p.Hq + hq) * p.nsplit + split_idx;
-        const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
+    // the partials reuse the K ring: every wave must be done with it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    float* red_o = reinterpret_cast<float*>(lds);     // [NW][16][D + 4]
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int m = 4 * q4 + k;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) red_o[(wave * 16 + lq) * (D + 4) + m * DB + db] = oacc[db][k];
+    }
+    if (q4 == 0) {
+        red_s[wave][0][lq] = m_run;
+        red_s[wave][1][lq] = l_tot;
+        red_s[wave][2][lq] = lr_tot;
+    }
+    __syncthreads();
+    // thread t: query t % 16, columns (t / 16) + 16*u
+    const int tq = threadIdx.x & 15, tc = threadIdx.x >> 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_s[w][0][tq]);
+    float wgt[NW], Lf = 0.f, Lr = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const float mw = red_s[w][0][tq];
+        wgt[w] = mw == -INFINITY ? 0.f : exp2_fast(mw - M);
+        Lf = fmaf(wgt[w], red_s[w][1][tq], Lf);
+        Lr = fmaf(wgt[w], red_s[w][2][tq], Lr);
+    }
+    const int tqh = 16 * qb + tq;
+    if (tqh < p.G) {
+        const int thq = hkv * p.G + tqh;
+        const long long row = ((long long)b * p.Hq + thq) * p.nsplit + split_idx;
+        const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
         float* orow = p.ws_o + row * D;
+        for (int col = tc; col < D; col += 64 * NW / 16) {
+            float acc = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int m = 4 * q4 + k;
-#pragma unroll
-            for (int d4 = 0; d4 < DB; d4 += 4)
-                *reinterpret_cast<f32x4*>(orow + m * DB + d4) =
-                    (f32x4){oacc[d4][k] * inv, oacc[d4 + 1][k] * inv, oacc[d4 + 2][k] * inv,
-                            oacc[d4 + 3][k] * inv};
+            for (int w = 0; w < NW; ++w) acc = fmaf(wgt[w], red_o[(w * 16 + tq) * (D + 4) + col], acc);
+            orow[col] = acc * inv;
         }
-        if (q4 == 0)
-            p.ws_lse[row] = l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
+        if (tc == 0)
+            p.ws_lse[row] = Lf > 0.f ? (M + log2_fast(Lf)) * kLn2 : -INFINITY;
     }
 }
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) {
     constexpr int PER = D / 64;        // columns per lane
+    constexpr int UNROLL = 32;         // partial rows in flight per lane
     const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (w >= p.B * p.Hq) return;
@@ -236,18 +334,46 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
     const int n = (L + p.split - 1) / p.split;
     const long long row0 = ((long long)b * p.Hq + hq) * p.nsplit;
 
+    // M = max_c LSE_c, lanes over splits
     float M = -INFINITY;
-    for (int s = 0; s < n; ++s) M = fmaxf(M, p.ws_lse[row0 + s]);
+    for (int s0 = 0; s0 < n; s0 += 64)
+        if (s0 + lane < n) M = fmaxf(M, p.ws_lse[row0 + s0 + lane]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+
     float acc[PER];
+#pragma unroll
     for (int u = 0; u < PER; ++u) acc[u] = 0.f;
     float sum = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < n; ++s) {
-            const float ls = p.ws_lse[row0 + s];
-            const float wgt = ls == -INFINITY ? 0.f : exp2_fast((ls - M) * kLog2e);
-            sum += wgt;
-            const float* src = p.ws_o + (row0 + s) * D + lane * PER;
-            for (int u = 0; u < PER; ++u) acc[u] = fmaf(wgt, src[u], acc[u]);
+        const float* src = p.ws_o + row0 * D + lane * PER;
+        for (int s0 = 0; s0 < n; s0 += 64) {
+            // lane s holds the weight of split s0 + s; the sums below run
+            // in split order (deterministic)
+            float wl = 0.f;
+            if (s0 + lane < n) {
+                const float ls = p.ws_lse[row0 + s0 + lane];
+                wl = ls == -INFINITY ? 0.f : exp2_fast((ls - M) * kLog2e);
+            }
+            const int m = min(64, n - s0);
+            for (int c0 = 0; c0 < m; c0 += UNROLL) {
+                float x[UNROLL][PER];
+#pragma unroll
+                for (int k = 0; k < UNROLL; ++k)
+#pragma unroll
+                    for (int u = 0; u < PER; ++u)
+                        x[k][u] = c0 + k < m ? src[(long long)(s0 + c0 + k) * D + u] : 0.f;
+#pragma unroll
+                for (int k = 0; k < UNROLL; ++k) {
+                    if (c0 + k < m) {
+                        const float wk = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), c0 + k));
+                        sum += wk;
+#pragma unroll
+                        for (int u = 0; u < PER; ++u) acc[u] = fmaf(wk, x[k][u], acc[u]);
+                    }
+                }
+            }
         }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
@@ -265,8 +391,8 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
 template <int D, bool BF16>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
     const long long nsplit_blocks = (long long)p.nsplit * p.qblocks * p.Hkv * p.B;
-    hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16>), dim3((unsigned)nsplit_blocks), dim3(64),
-                       0, s, p);
+    hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16>), dim3((unsigned)nsplit_blocks),
+                       dim3(kDecodeThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long ncomb = ((long long)p.B * p.Hq + 3) / 4;

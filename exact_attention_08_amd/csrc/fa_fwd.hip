@@ -71,7 +71,6 @@ struct FwdGeo {
 };
 
 constexpr float kRescaleThreshold = 8.0f;       // log2 units
-constexpr int kFwdThreads = 512;                // 8 waves
 static_assert(FwdGeo<128>::NW * 64 == kFwdThreads && FwdGeo<64>::NW * 64 == kFwdThreads, "block size");
 
 typedef __attribute__((address_space(3))) short lds_short;

@@ -54,7 +54,10 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStre
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 
 // Kernel tile geometry, shared with the host for grid sizing.
-constexpr int kFwdBM = 256;     // query rows per work-group (4 waves x 64)
+constexpr int kFwdBM = 256;        // query rows per work-group (8 waves x 32)
+constexpr int kFwdThreads = 512;   // forward work-group size
+constexpr int kDecodeWaves = 4;    // waves per decode split work-group
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr float kLog2e_host = 1.4426950408889634f;
 
 }  // namespace fa

@@ -95,6 +95,7 @@ DECODE_CASES = [
     ("window_left", 3, 8, 2, 3000, [3000, 100, 1500], 128, "bf16", True, (200, -1), 512, 305),
     ("d64_fp16", 3, 16, 4, 1200, [1200, 1, 640], 64, "fp16", True, (-1, -1), 256, 306),
     ("empty_cache_row", 2, 4, 1, 300, [0, 300], 128, "bf16", True, (-1, -1), 128, 307),
+    ("split192_window", 2, 8, 2, 2000, [1999, 700], 128, "bf16", True, (300, -1), 192, 308),
 ]
 
 
