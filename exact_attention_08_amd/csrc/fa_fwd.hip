@@ -33,8 +33,9 @@
 //     read a 4-key x 16-column block and each lane receives one column), so
 //     each V^T operand half is one contiguous 512-byte wave read.
 // Contiguous wave reads are bank-conflict free.  K and V are buffered in LDS
-// in a ring of STAGES tiles each, so loads are issued STAGES-1 tiles ahead of
-// use; one barrier per tile.
+// in a ring of STAGES tiles each; loads are issued in pairs of tiles, 5 to 6
+// tiles ahead of use, and one barrier per pair of tiles both publishes the
+// next pair's data and frees the ring slots for the next copies.
 //
 // Pipelining.  While the softmax of tile j runs on the VALU, the MFMAs of
 // S(j+1) = K_{j+1} Q^T are already issued; the row max of tile j+1 is taken
@@ -68,6 +69,7 @@ struct FwdGeo {
     static constexpr int LPS = 2 * TILE_BLOCKS / NW;            // DMA loads per wave per step
     static_assert((2 * TILE_BLOCKS) % NW == 0, "the blocks of a step split evenly over the waves");
     static_assert((STAGES & (STAGES - 1)) == 0, "ring depth must be a power of two");
+    static_assert(STAGES >= 6, "pairs of tiles need two sets in flight");
 };
 
 constexpr float kRescaleThreshold = 8.0f;       // log2 units
@@ -221,8 +223,9 @@ void fa_fwd_kernel(FwdParams p) {
     auto vslot = [&](int jt) __attribute__((always_inline)) {
         return v_ring + ((jt - tile_lo) & (T::STAGES - 1)) * TE;
     };
-    // Load set of step s: K_s and V_{s-1}.  Step j issues set j + STAGES,
-    // which refills the slots of K_j and V_{j-1} (both consumed by step j-1).
+    // Load set of step s: K_s and V_{s-1}.  Set s refills the slots of
+    // K_{s-STAGES} and V_{s-1-STAGES}, both last read in step s-STAGES-1
+    // (step -1 being the first tile's Q.K product before the loop).
     auto issue = [&](int s) __attribute__((always_inline)) {
         const i32x4 krs = tile_rsrc(kseq, s), vrs = tile_rsrc(vseq, s - 1);
         const uint32_t kdst = lds_addr(kslot(s)), vdst = lds_addr(vslot(s - 1));
@@ -234,13 +237,18 @@ void fa_fwd_kernel(FwdParams p) {
                 dma16_to_lds(vrs, vdst + dma_loff[i], dma_voff[i], 0);
         }
     };
-    // Before step j the sets up to j+1 (K_{j+1}, V_j) must have landed in
-    // every wave; the STAGES-2 sets issued after it may still be in flight.
-    // The wait and the barrier form one asm statement so that no LDS access
-    // is moved across them.
-    auto sync_tile = [&]() __attribute__((always_inline)) {
+    // Steps run in pairs (relative steps 2k, 2k+1).  The even step issues
+    // sets 2k+STAGES-2 and 2k+STAGES-1; the odd step ends with a barrier
+    // after which every wave has finished step 2k+1, so the next pair's
+    // copies only refill slots last read at step 2k or earlier.  Steps
+    // 2k+2, 2k+3 read sets 2k+3, 2k+4 (K_{j+1}, V_j), so before that
+    // barrier each wave waits until its copies up to set 2k+4 have landed:
+    // the STAGES-5 sets issued after it may still be in flight.  The wait and
+    // the barrier form one asm statement so that no LDS access is moved
+    // across them.
+    auto sync_pair = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
-                     ::"n"(T::LPS * (T::STAGES - 2)) : "memory");
+                     ::"n"(T::LPS * (T::STAGES - 5)) : "memory");
     };
 
     // ---- the wave's 32 query rows as MFMA B operands ---------------------
@@ -372,9 +380,12 @@ void fa_fwd_kernel(FwdParams p) {
 
     // One tile step.  On entry tile j's scores (scur) carry their final row
     // max; K_{j+1} and V_j are in the ring.
-    auto step = [&](f32x16 (&scur)[T::NB], f32x16 (&snext)[T::NB], int j)
+    auto step = [&](f32x16 (&scur)[T::NB], f32x16 (&snext)[T::NB], int j, bool even)
         __attribute__((always_inline)) {
-        issue(j + T::STAGES);
+        if (even) {
+            issue(j + T::STAGES - 2);
+            issue(j + T::STAGES - 1);
+        }
         if (j >= fast_lo && j <= fast_hi) {
             // steady state: one straight-line block
             qk(snext, kslot(j + 1));
@@ -390,21 +401,23 @@ void fa_fwd_kernel(FwdParams p) {
             }
             if (pn) rowmax(snext, j + 1, !interior(j + 1));
         }
-        sync_tile();
+        if (!even) sync_pair();
     };
 
     if (ntiles > 0) {
-        for (int s = tile_lo; s < tile_lo + T::STAGES; ++s) issue(s);
-        sync_tile();
+        // sets 0 .. STAGES-3; the first pair of steps reads sets 0 .. 2
+        for (int s = tile_lo; s < tile_lo + T::STAGES - 2; ++s) issue(s);
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
+                     ::"n"(T::LPS * (T::STAGES - 5)) : "memory");
         if (part(tile_lo)) {
             qk(sacc[0], kslot(tile_lo));
             rowmax(sacc[0], tile_lo, !interior(tile_lo));
         }
         // unrolled by two so that the score buffers swap roles statically
         for (int r = 0; r < ntiles; r += 2) {
-            step(sacc[0], sacc[1], tile_lo + r);
+            step(sacc[0], sacc[1], tile_lo + r, true);
             if (r + 1 >= ntiles) break;
-            step(sacc[1], sacc[0], tile_lo + r + 1);
+            step(sacc[1], sacc[0], tile_lo + r + 1, false);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // DMA loads of unused sets still in flight
