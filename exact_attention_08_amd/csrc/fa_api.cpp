@@ -103,7 +103,9 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     p.cu_q = nullptr; p.cu_k = nullptr;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk;
-    p.nqt = (Sq + fa::kFwdBM - 1) / fa::kFwdBM;
+    p.gw = fa::fwd_heads_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.nqt = (Sq + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;
     p.lse_b_stride = (long long)Hq * Sq;
@@ -111,7 +113,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
     set_scale(softmax_scale, &p.c, &p.qsign);
     p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
-    if ((long long)p.nqt * Hq * B * fa::kFwdThreads > kMaxGridThreads)
+    if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
     return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
 }
@@ -138,7 +140,9 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out
     p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = max_seqlen_q; p.Sk = max_seqlen_k;
-    p.nqt = (max_seqlen_q + fa::kFwdBM - 1) / fa::kFwdBM;
+    p.gw = fa::fwd_heads_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.nqt = (max_seqlen_q + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;
     p.lse_b_stride = 0;
@@ -146,7 +150,7 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out
     p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
     set_scale(softmax_scale, &p.c, &p.qsign);
     p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
-    if ((long long)p.nqt * Hq * B * fa::kFwdThreads > kMaxGridThreads)
+    if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
     return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, true, stream));
 }

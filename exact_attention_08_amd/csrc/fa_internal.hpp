@@ -27,6 +27,8 @@ struct FwdParams {
     float c;                    // |scale| * log2(e)
     uint32_t qsign;             // 0x80008000 when scale < 0 (q negated exactly), else 0
     int xcd_groups;             // (B*Hkv)/8 when B*Hkv % 8 == 0, else 0 (no remap)
+    int gw;                     // query heads per work-group (fwd_heads_per_wg(G))
+    int bm;                     // query rows per work-group (fwd_rows_per_wg(G))
 };
 
 // Decode split kernel + combine kernel.
@@ -54,8 +56,14 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStre
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 
 // Kernel tile geometry, shared with the host for grid sizing.
-constexpr int kFwdBM = 256;        // query rows per work-group (8 waves x 32)
-constexpr int kFwdThreads = 512;   // forward work-group size
+constexpr int kFwdWaveRows = 64;   // query rows per forward wave
+constexpr int kFwdWaves = 4;       // waves per forward work-group (one per SIMD)
+constexpr int kFwdThreads = 64 * kFwdWaves;
+// A forward work-group covers gw query heads that share one K/V head (the
+// largest of 4, 2, 1 dividing G) and 64 * 4 / gw query rows, so its waves
+// need the same K/V tiles at the same steps.
+inline int fwd_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+inline int fwd_rows_per_wg(int G) { return kFwdWaveRows * kFwdWaves / fwd_heads_per_wg(G); }
 constexpr int kDecodeWaves = 4;    // waves per decode split work-group
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr float kLog2e_host = 1.4426950408889634f;
