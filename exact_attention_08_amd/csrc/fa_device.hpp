@@ -97,6 +97,25 @@ __device__ __forceinline__ float xor32(float x) {
     return __builtin_bit_cast(float, lower ? r[1] : r[0]);
 }
 
+// max / sum of x over lanes l and l^32, the same value in both lanes.
+// Swapping x with itself leaves one register holding the lower half's
+// values in every lane and the other the upper half's (one v_permlane32_swap,
+// no lane select); the operands are in the same order in every lane.  (The
+// two results are copied out as scalars first: a bit_cast applied directly
+// to an element of the returned pair read the wrong element.)
+__device__ __forceinline__ float max_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
 __device__ __forceinline__ bool wave_any(bool p) {
     return __builtin_amdgcn_ballot_w64(p) != 0ull;
 }

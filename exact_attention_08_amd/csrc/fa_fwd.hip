@@ -370,7 +370,7 @@ void fa_fwd_kernel(FwdParams p) {
         for (int q4 = 0; q4 < 4; ++q4)
             m4[q4] = fmaxf(fmaxf(s[4 * q4], s[4 * q4 + 1]), fmaxf(s[4 * q4 + 2], s[4 * q4 + 3]));
         float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        mx = fmaxf(mx, xor32(mx));
+        mx = max_halves(mx);
         const float mnew = fmaxf(m_run[h], mx * c);    // -inf stays -inf (c > 0)
         // Per-row decision (rows are independent); the branch only skips the
         // work when no row of the wave needs it.  Rows keeping their max are
@@ -391,19 +391,28 @@ void fa_fwd_kernel(FwdParams p) {
     // P = exp2(S*c - m) as 16-bit B operands; masked scores are -inf -> 0
     auto softmax_exp = [&](int h) __attribute__((always_inline)) {
         const float m_use = m_run[h] == -INFINITY ? 0.f : m_run[h];
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = exp2_fast(fmaf(sacc[h][e], c, -m_use));
+        // two normalisers: O is divided by the sum of the 16-bit weights
+        // actually fed to P.V (so its weights sum to one); LSE uses the sum
+        // of the fp32 values (16-bit rounding would bias it by up to 2^-9).
+        // Both are summed as trees: with one wave per SIMD a serial chain of
+        // dependent adds would stall the wave.
+        float lr2[2] = {0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-            const float x0 = exp2_fast(fmaf(sacc[h][e], c, -m_use));
-            const float x1 = exp2_fast(fmaf(sacc[h][e + 1], c, -m_use));
-            const uint32_t pk = pack2<BF16>(x0, x1);
+            const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
             // element e is slot (e & 7) of reduction step e >> 3
             pb[h][e >> 3][(e & 7) >> 1] = pk;
-            // two normalisers: O is divided by the sum of the 16-bit weights
-            // actually fed to P.V (so its weights sum to one); LSE uses the sum
-            // of the fp32 values (16-bit rounding would bias it by up to 2^-9)
-            l_run[h] += x0 + x1;
-            lr_run[h] = dot2_ones<BF16>(pk, lr_run[h]);
+            lr2[(e >> 1) & 1] = dot2_ones<BF16>(pk, lr2[(e >> 1) & 1]);
         }
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int e = 0; e < w; ++e) x[e] += x[e + w];
+        l_run[h] += x[0];
+        lr_run[h] += lr2[0] + lr2[1];
     };
     auto pv = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
@@ -427,14 +436,19 @@ void fa_fwd_kernel(FwdParams p) {
         pv(0);
         rowmax(1, jt, masked);
     };
-    auto step = [&](int jt, bool even) __attribute__((always_inline)) {
+    // A step with new tile jt: copies (even steps), the body, the barrier
+    // (odd steps).  Steps that need a mask (or compute nothing) run in the
+    // loops before and after the unmasked run, so the unmasked loop body is
+    // straight-line code.
+    auto step = [&](int jt, bool even, bool fast) __attribute__((always_inline)) {
         if (even) {
             issue(jt + T::STAGES - 2);
             issue(jt + T::STAGES - 1);
         }
-        // one copy of the body (the mask is a small branch inside it), so the
-        // accumulators keep their registers across the step
-        if (jt >= act_lo && jt <= act_hi) body(jt, jt < fast_lo || jt > fast_hi);
+        if (fast)
+            body(jt, false);
+        else if (jt >= act_lo && jt <= act_hi)
+            body(jt, true);
         if (!even) sync_pair();
     };
 
@@ -451,15 +465,17 @@ void fa_fwd_kernel(FwdParams p) {
         // sets 0 .. STAGES-3; the first pair of steps reads sets 0 and 1
         for (int s = tile_lo; s < tile_lo + T::STAGES - 2; ++s) issue(s);
         sync_pair();
-        // steps for new tiles tile_lo .. tile_last + 1 (the last one only
-        // finishes half B), unrolled by two for the static pairing (no exit
-        // inside the pair: the accumulators then keep their registers)
+        // steps r = 0 .. ntiles (new tile tile_lo + r; the last one only
+        // finishes half B); the unmasked ones [rf_lo, rf_hi] run two per
+        // iteration (static parity), starting at an even step
+        const int rf_lo = max(fast_lo - tile_lo, 0), rf_hi = fast_hi - tile_lo;
         int r = 0;
-        for (; r + 1 <= ntiles; r += 2) {
-            step(tile_lo + r, true);
-            step(tile_lo + r + 1, false);
+        for (; r < rf_lo || (r <= rf_hi && (r & 1)); ++r) step(tile_lo + r, (r & 1) == 0, false);
+        for (; r + 1 <= rf_hi; r += 2) {
+            step(tile_lo + r, true, true);
+            step(tile_lo + r + 1, false, true);
         }
-        if (r <= ntiles) step(tile_lo + r, true);
+        for (; r <= ntiles; ++r) step(tile_lo + r, (r & 1) == 0, false);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // DMA loads of unused sets still in flight
 
@@ -469,8 +485,8 @@ void fa_fwd_kernel(FwdParams p) {
         sq * tok_bytes_q, 0x00020000);          // rows past the sequence are dropped
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const float l_tot = l_run[h] + xor32(l_run[h]);
-        const float lr_tot = lr_run[h] + xor32(lr_run[h]);
+        const float l_tot = sum_halves(l_run[h]);
+        const float lr_tot = sum_halves(lr_run[h]);
         const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
         const int row = r0[h] + lq;
 #pragma unroll
