@@ -96,6 +96,10 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// Make v count as used here, so that its computation stays before this
+// point (an empty asm statement the scheduler keeps in order).
+__device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
+
 // Keep an MFMA operand in the accumulation registers: MFMAs read A and B
 // operands from there directly (and LDS / buffer loads write there
 // directly, so this folds into the load).  The 256 architectural VGPRs then
@@ -352,7 +356,25 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) sacc[h] = mfma32x32x16<BF16>(kreg[ks], qreg[h][ks], sacc[h]);
     };
-    // row max of half h's tile jt (masking it first when needed) and the
+    // lazy rescale of half h after its tile max mnew (log2 units).
+    // Per-row decision (rows are independent); the branch only skips the
+    // work when no row of the wave needs it.  Rows keeping their max are
+    // multiplied by exactly 1.
+    auto rescale = [&](int h, float mnew) __attribute__((always_inline)) {
+        const bool raise = mnew > m_run[h] + kRescaleThreshold;
+        if (wave_any(raise)) {
+            asm volatile("");   // keep this rare block a real branch (not speculated)
+            const float alpha = raise ? exp2_fast(m_run[h] - mnew) : 1.f;
+            l_run[h] *= alpha;
+            lr_run[h] *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[h][db][e] *= alpha;
+            m_run[h] = raise ? mnew : m_run[h];
+        }
+    };
+    // row max of half h's tile jt (masking it first when needed), then the
     // lazy rescale
     auto rowmax = [&](int h, int jt, bool masked) __attribute__((always_inline)) {
         f32x16& s = sacc[h];
@@ -371,22 +393,7 @@ void fa_fwd_kernel(FwdParams p) {
             m4[q4] = fmaxf(fmaxf(s[4 * q4], s[4 * q4 + 1]), fmaxf(s[4 * q4 + 2], s[4 * q4 + 3]));
         float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         mx = max_halves(mx);
-        const float mnew = fmaxf(m_run[h], mx * c);    // -inf stays -inf (c > 0)
-        // Per-row decision (rows are independent); the branch only skips the
-        // work when no row of the wave needs it.  Rows keeping their max are
-        // multiplied by exactly 1.
-        const bool raise = mnew > m_run[h] + kRescaleThreshold;
-        if (wave_any(raise)) {
-            asm volatile("");   // keep this rare block a real branch (not speculated)
-            const float alpha = raise ? exp2_fast(m_run[h] - mnew) : 1.f;
-            l_run[h] *= alpha;
-            lr_run[h] *= alpha;
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[h][db][e] *= alpha;
-            m_run[h] = raise ? mnew : m_run[h];
-        }
+        rescale(h, fmaxf(m_run[h], mx * c));           // -inf stays -inf (c > 0)
     };
     // P = exp2(S*c - m) as 16-bit B operands; masked scores are -inf -> 0
     auto softmax_exp = [&](int h) __attribute__((always_inline)) {
@@ -422,6 +429,81 @@ void fa_fwd_kernel(FwdParams p) {
                 oacc[h][db] = mfma32x32x16<BF16>(vreg[kk][db], pb[h][kk], oacc[h][db]);
     };
 
+    // One half-step of the unmasked body in a fixed instruction order: the
+    // S MFMAs of half hs interleaved with the exponentials of half hp, then
+    // half hp's P.V MFMAs interleaved with its sums and half hs's row max.
+    // With one wave per SIMD the matrix and vector pipes only overlap as far
+    // as the instruction stream alternates them, so sched_barrier(0) fences
+    // keep this order.
+    auto region = [&](int hs, int hp) __attribute__((always_inline)) {
+        constexpr int EPK = 16 / T::KS;                 // exponentials per S MFMA
+        const float m_use = m_run[hp] == -INFINITY ? 0.f : m_run[hp];
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[hs][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) {
+            sacc[hs] = mfma32x32x16<BF16>(kreg[ks], qreg[hs][ks], sacc[hs]);
+#pragma unroll
+            for (int j = 0; j < EPK; ++j) {
+                const int e = ks * EPK + j;
+                x[e] = exp2_fast(fmaf(sacc[hp][e], c, -m_use));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) pb[hp][e >> 3][(e & 7) >> 1] = pack2<BF16>(x[e], x[e + 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        // P.V of half hp; beside it: 8 v_dot2 (16-bit sum), 15 adds (fp32
+        // sum tree), then half hs's row max once its S MFMAs have drained
+        float lr2[2] = {0.f, 0.f};
+        float m4[4];
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < T::KK * T::DB; ++i) {
+            const int kk = i / T::DB, db = i % T::DB;
+            oacc[hp][db] = mfma32x32x16<BF16>(vreg[kk][db], pb[hp][kk], oacc[hp][db]);
+            // (the sums are pinned to their slot: left alone the compiler
+            // sinks them to their next use, outside this interleave)
+            if (i == 0) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) lr2[u & 1] = dot2_ones<BF16>(pb[hp][u >> 2][u & 3], lr2[u & 1]);
+                pin(lr2[0]); pin(lr2[1]);
+            } else if (i == 1) {
+#pragma unroll
+                for (int u = 4; u < 8; ++u) lr2[u & 1] = dot2_ones<BF16>(pb[hp][u >> 2][u & 3], lr2[u & 1]);
+                lr_run[hp] += lr2[0] + lr2[1];
+                pin(lr_run[hp]);
+            } else if (i == 2) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] += x[e + 8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pin(x[e]);
+            } else if (i == 3) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] += x[e + 4];
+                x[0] += x[2]; x[1] += x[3];
+                l_run[hp] += x[0] + x[1];
+                pin(l_run[hp]);
+            } else if (i == T::KK * T::DB - 3) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    m4[q4] = fmaxf(fmaxf(sacc[hs][4 * q4], sacc[hs][4 * q4 + 1]),
+                                   fmaxf(sacc[hs][4 * q4 + 2], sacc[hs][4 * q4 + 3]));
+            } else if (i == T::KK * T::DB - 2) {
+                mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rescale(hs, fmaxf(m_run[hs], mx * c));
+    };
+    auto body_fast = [&](int jt) __attribute__((always_inline)) {
+        load_k(kslot(jt));
+        region(0, 1);
+        load_v(vslot(jt));
+        region(1, 0);
+    };
+
     // Step with new tile jt (see the pipeline above).  On entry half B's
     // scores of tile jt-1 carry their final row max and V_{jt-1} is in vreg.
     auto body = [&](int jt, bool masked) __attribute__((always_inline)) {
@@ -446,7 +528,7 @@ void fa_fwd_kernel(FwdParams p) {
             issue(jt + T::STAGES - 1);
         }
         if (fast)
-            body(jt, false);
+            body_fast(jt);
         else if (jt >= act_lo && jt <= act_hi)
             body(jt, true);
         if (!even) sync_pair();
