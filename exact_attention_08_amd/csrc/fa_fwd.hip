@@ -562,15 +562,20 @@ void fa_fwd_kernel(FwdParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // DMA loads of unused sets still in flight
 
     // ---- epilogue: normalise once, write O and LSE -----------------------
-    const auto ors = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((char*)p.o + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2), (short)0,
-        sq * tok_bytes_q, 0x00020000);          // rows past the sequence are dropped
+    // O goes through LDS so that every store writes whole rows: in the
+    // accumulator layout a store instruction would cover 16 bytes of each of
+    // 32 rows.  Each wave stages its 64 x D tile in its own part of the
+    // (now idle) K ring, rows of D/8 16-byte chunks with chunk c of row r at
+    // c ^ (r % (D/8)) (conflict-free reads), then stores D/8 lanes per row.
+    constexpr int CH = D / 8;                  // 16-byte chunks per row
+    asm volatile("s_barrier" ::: "memory");    // every wave is done with the ring
+    char* stage = reinterpret_cast<char*>(k_ring) + wave * (T::WR * D * 2);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const float l_tot = sum_halves(l_run[h]);
         const float lr_tot = sum_halves(lr_run[h]);
         const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
-        const int row = r0[h] + lq;
+        const int r = T::HR * h + lq;          // row within the wave's tile
 #pragma unroll
         for (int db = 0; db < T::DB; ++db)
 #pragma unroll
@@ -578,15 +583,27 @@ void fa_fwd_kernel(FwdParams p) {
                 u32x2 w;
                 w.x = pack2<BF16>(oacc[h][db][4 * jj + 0] * inv, oacc[h][db][4 * jj + 1] * inv);
                 w.y = pack2<BF16>(oacc[h][db][4 * jj + 2] * inv, oacc[h][db][4 * jj + 3] * inv);
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    w, ors, row * tok_bytes_q + (32 * db + 8 * jj + 4 * g) * 2, 0, 0);
+                const int chunk = (4 * db + jj) ^ (r % CH);   // columns 32db + 8jj .. +7
+                *reinterpret_cast<u32x2*>(stage + r * (2 * D) + chunk * 16 + 8 * g) = w;
             }
+        const int row = r0[h] + lq;
         if (p.lse != nullptr && g == 0 && row < sq) {
             const long long row_base = VARLEN ? q_tok0 : 0;
             const float lse = l_tot > 0.f ? (m_run[h] + log2_fast(l_tot)) * kLn2 : -INFINITY;
             p.lse[(long long)b * p.lse_b_stride + (long long)hq * p.lse_h_stride + row_base + row] =
                 lse;
         }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's own staging writes
+    const auto ors = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((char*)p.o + (q_tok0 * p.q_tok_stride + (long long)hq * D) * 2), (short)0,
+        sq * tok_bytes_q, 0x00020000);          // rows past the sequence are dropped
+    constexpr int RPI = 64 / CH;               // rows per store instruction
+#pragma unroll
+    for (int i = 0; i < T::WR / RPI; ++i) {
+        const int r = RPI * i + lane / CH, c = lane % CH;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (2 * D) + ((c ^ (r % CH)) * 16));
+        __builtin_amdgcn_raw_buffer_store_b128(x, ors, (r0[0] + r) * tok_bytes_q + c * 16, 0, 0);
     }
 }
 
