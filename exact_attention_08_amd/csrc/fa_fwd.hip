@@ -27,15 +27,15 @@
 // product O^T = V^T P^T: P never leaves registers.
 //
 // Software pipeline.  With one wave per SIMD the overlap of matrix and
-// vector work has to come from one instruction stream, so the two halves
-// run half a tile apart.  The step with new tile t is four phases, each
-// pairing the MFMAs of one half with the vector work of the other:
-//     P1: S_A(t)   = K_t Q_A^T        ||  P_B(t-1) = exp2(S_B(t-1) c - m_B)
-//     P2: O_B     += V_{t-1}^T P_B^T  ||  row max of S_A(t)
-//     P3: S_B(t)   = K_t Q_B^T        ||  P_A(t)   = exp2(S_A(t) c - m_A)
-//     P4: O_A     += V_t^T P_A^T      ||  row max of S_B(t)
-// K_t is read from LDS once (P1) and kept in registers for P3; V_t is read
-// once (P4) and kept for P2 of the next step.
+// vector work has to come from one instruction stream.  The step with new
+// tile t is two regions, one per half h (A, then B), each with 16 MFMA
+// slots: the 8 MFMAs of S_h(t) = K_t Q_h^T, then the 8 of O_h += V_{t-1}
+// P_h(t-1) (P from the region before); beside them, one exponential per
+// slot, the weights P of the other half's newest tile (S from the region
+// before) are computed, packed and summed.  No slot waits for a result of
+// its own region.  K_t and V_{t-1} serve both regions; K_{t+1} and V_t are
+// read from LDS during step t (one read per slot) into the other half of
+// double-buffered operand registers.
 //
 // Data movement.  K and V tiles go from HBM/L2 straight into LDS with
 // bounds-checked buffer loads (buffer_load_dwordx4 ... lds): rows past the
@@ -50,15 +50,18 @@
 //     read a 4-key x 16-column block and each lane receives one column), so
 //     each V^T operand half is one contiguous 512-byte wave read.
 // Contiguous wave reads are bank-conflict free.  K and V are buffered in LDS
-// in a ring of STAGES tiles; copies are issued in pairs of tiles, 6 tiles
-// ahead, and one barrier per pair of steps both publishes the next tiles
-// and frees ring slots for the next copies.
+// in a ring of STAGES tiles; each step copies one tile 6 tiles ahead (its
+// copies spread over the MFMA slots), and one barrier per pair of steps
+// both publishes the next tiles and frees ring slots for the next copies.
 //
 // Online softmax in base 2: scores are scaled by c = |scale|*log2(e) inside
 // one FMA feeding v_exp_f32.  A row's running max is raised only when its
 // tile max exceeds it by more than 8 (log2 units); until then the stale max
 // is kept, which is exact because the same max is used for the numerator,
-// the sum and the final LSE, and it skips most rescales of O.  O is normalised
+// the sum and the final LSE, and it skips most rescales of O.  A tile is
+// exponentiated with the stale max first; only when a lane's sum of weights
+// exceeds 2^8 (or a row has no max yet) is the true tile max taken and the
+// tile redone, so unmasked steps compute no row max at all.  O is normalised
 // by the sum of the 16-bit probabilities fed to P.V (v_dot2 against (1, 1)),
 // LSE by the fp32 sum.
 #include "fa_device.hpp"
@@ -81,11 +84,16 @@ struct FwdGeo {
     static constexpr int LPS = 2 * TILE_BLOCKS / NW;            // DMA loads per wave per set
     static_assert((2 * TILE_BLOCKS) % NW == 0, "the blocks of a set split evenly over the waves");
     static_assert((STAGES & (STAGES - 1)) == 0, "ring depth must be a power of two");
-    static_assert(STAGES >= 6, "pairs of steps need two sets in flight");
+    static_assert(STAGES >= 7, "pairs of steps need two sets in flight");
 };
 
 constexpr float kRescaleThreshold = 8.0f;       // log2 units
 static_assert(FwdGeo<128>::WR == kFwdWaveRows && FwdGeo<128>::NW * 64 == kFwdThreads, "block size");
+
+template <int V>
+struct int_c {
+    static constexpr int value = V;
+};
 
 typedef __attribute__((address_space(3))) short lds_short;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -99,6 +107,7 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
 // Make v count as used here, so that its computation stays before this
 // point (an empty asm statement the scheduler keeps in order).
 __device__ __forceinline__ void pin(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void pin_u(uint32_t v) { asm volatile("" ::"v"(v)); }
 
 // Keep an MFMA operand in the accumulation registers: MFMAs read A and B
 // operands from there directly (and LDS / buffer loads write there
@@ -263,28 +272,36 @@ void fa_fwd_kernel(FwdParams p) {
     auto vslot = [&](int jt) __attribute__((always_inline)) {
         return v_ring + ((jt - tile_lo) & (T::STAGES - 1)) * TE;
     };
-    auto issue = [&](int s) __attribute__((always_inline)) {
-        const i32x4 krs = tile_rsrc(kseq, s), vrs = tile_rsrc(vseq, s);
-        const uint32_t kdst = lds_addr(kslot(s)), vdst = lds_addr(vslot(s));
-#pragma unroll
-        for (int i = 0; i < T::LPS; ++i) {
-            if (dma_k[i])
-                dma16_to_lds(krs, kdst + dma_loff[i], dma_voff[i], 0);
-            else
-                dma16_to_lds(vrs, vdst + dma_loff[i], dma_voff[i], 0);
-        }
+    // copy i (of LPS) of this wave for set s
+    struct SetCopy {
+        i32x4 krs, vrs;
+        uint32_t kdst, vdst;
     };
-    // Step w (relative to tile_lo) reads set w only, and set s + STAGES
-    // refills the slots of set s, so it may be issued once every wave has
-    // finished step s.  Steps run in pairs (2k, 2k+1): the even step issues
-    // sets 2k+STAGES-2 and 2k+STAGES-1; the odd step ends with a barrier.
-    // Before that barrier each wave waits until its copies of the sets read
-    // by the next pair (2k+2, 2k+3) have landed; the STAGES-4 sets issued
-    // after them may still be in flight.  The wait and the barrier form one
-    // asm statement so that no LDS access is moved across them.
+    auto set_copy = [&](int s) __attribute__((always_inline)) {
+        return SetCopy{tile_rsrc(kseq, s), tile_rsrc(vseq, s), lds_addr(kslot(s)), lds_addr(vslot(s))};
+    };
+    auto copy_one = [&](const SetCopy& sc, int i) __attribute__((always_inline)) {
+        if (dma_k[i])
+            dma16_to_lds(sc.krs, sc.kdst + dma_loff[i], dma_voff[i], 0);
+        else
+            dma16_to_lds(sc.vrs, sc.vdst + dma_loff[i], dma_voff[i], 0);
+    };
+    auto issue = [&](int s) __attribute__((always_inline)) {
+        const SetCopy sc = set_copy(s);
+#pragma unroll
+        for (int i = 0; i < T::LPS; ++i) copy_one(sc, i);
+    };
+    // Step w (relative to tile_lo) reads K of set w+1 and V of set w (and
+    // K of set w itself when it needs masks), and set s + STAGES refills the
+    // slots of set s, so it may be issued once every wave has finished step
+    // s.  Step w issues set w+STAGES-2; steps run in pairs (2k, 2k+1) and the
+    // odd step ends with a barrier.  Before that barrier each wave waits
+    // until its copies of the sets read by the next pair (2k+2 .. 2k+4) have
+    // landed; the STAGES-5 sets issued after them may still be in flight.  The wait and the barrier form one asm
+    // statement so that no LDS access is moved across them.
     auto sync_pair = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
-                     ::"n"(T::LPS * (T::STAGES - 4)) : "memory");
+                     ::"n"(T::LPS * (T::STAGES - 5)) : "memory");
     };
 
     // ---- the wave's 2 x 32 query rows as MFMA B operands ------------------
@@ -330,234 +347,266 @@ void fa_fwd_kernel(FwdParams p) {
 
     f32x16 sacc[2];                            // S^T of each half
     u32x4 pb[2][T::KK];                        // P of each half as 16-bit B operands
-    u32x4 kreg[T::KS];                         // K_t operands (P1 and P3)
-    u32x4 vreg[T::KK][T::DB];                  // V_t operands (P4, then P2 of the next step)
+    u32x4 kbuf[2][T::KS];                      // K operands, by step parity
+    u32x4 vbuf[2][T::KK][T::DB];               // V operands, by step parity
 
-    // ---- phases ----------------------------------------------------------
-    auto load_k = [&](const uint16_t* kt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks)
-            kreg[ks] = in_acc_regs(*reinterpret_cast<const u32x4*>(kt + ks * 512 + lane * 8));
+    // ---- operand loads from the LDS ring ----------------------------------
+    auto k_load = [&](const uint16_t* kt, int ks) __attribute__((always_inline)) {
+        return *reinterpret_cast<const u32x4*>(kt + ks * 512 + lane * 8);
     };
-    auto load_v = [&](const uint16_t* vt) __attribute__((always_inline)) {
-#pragma unroll
-        for (int kk = 0; kk < T::KK; ++kk)
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db) {
-                const uint16_t* base = vt + ((2 * kk) * T::DB + db) * 256 + lane * 4;
-                const u32x2 lo = ds_read_tr16(base);                    // keys 16kk + 4g + 0..3
-                const u32x2 hi = ds_read_tr16(base + T::DB * 256);      // keys 16kk + 8 + 4g + 0..3
-                vreg[kk][db] = in_acc_regs((u32x4){lo.x, lo.y, hi.x, hi.y});
-            }
+    // half hh (keys 16kk + 8hh + 4g + 0..3) of V^T operand (kk, db)
+    auto v_half = [&](const uint16_t* vt, int q, int hh) __attribute__((always_inline)) {
+        const int kk = q / T::DB, db = q % T::DB;
+        return ds_read_tr16(vt + ((2 * kk + hh) * T::DB + db) * 256 + lane * 4);
     };
-    auto qk = [&](int h) __attribute__((always_inline)) {
+    auto load_k_now = [&](const uint16_t* kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[h][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) sacc[h] = mfma32x32x16<BF16>(kreg[ks], qreg[h][ks], sacc[h]);
+        for (int ks = 0; ks < T::KS; ++ks) kbuf[0][ks] = in_acc_regs(k_load(kt, ks));
     };
-    // lazy rescale of half h after its tile max mnew (log2 units).
-    // Per-row decision (rows are independent); the branch only skips the
-    // work when no row of the wave needs it.  Rows keeping their max are
-    // multiplied by exactly 1.
-    auto rescale = [&](int h, float mnew) __attribute__((always_inline)) {
-        const bool raise = mnew > m_run[h] + kRescaleThreshold;
-        if (wave_any(raise)) {
-            asm volatile("");   // keep this rare block a real branch (not speculated)
-            const float alpha = raise ? exp2_fast(m_run[h] - mnew) : 1.f;
-            l_run[h] *= alpha;
-            lr_run[h] *= alpha;
+    auto load_v_now = [&](const uint16_t* vt) __attribute__((always_inline)) {
 #pragma unroll
-            for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[h][db][e] *= alpha;
-            m_run[h] = raise ? mnew : m_run[h];
+        for (int q = 0; q < T::KK * T::DB; ++q) {
+            const u32x2 lo = v_half(vt, q, 0), hi = v_half(vt, q, 1);
+            vbuf[1][q / T::DB][q % T::DB] = in_acc_regs((u32x4){lo.x, lo.y, hi.x, hi.y});
         }
     };
-    // row max of half h's tile jt (masking it first when needed), then the
-    // lazy rescale
-    auto rowmax = [&](int h, int jt, bool masked) __attribute__((always_inline)) {
-        f32x16& s = sacc[h];
-        if (masked) {
-            const int lo = rel_lo[h] - jt * T::BN, hi = rel_hi[h] - jt * T::BN;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int off = 8 * (e >> 2) + (e & 3);
-                s[e] = (off >= lo && off <= hi) ? s[e] : -INFINITY;
-            }
-        }
-        // tree reduction (short dependency chain)
-        float m4[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            m4[q4] = fmaxf(fmaxf(s[4 * q4], s[4 * q4 + 1]), fmaxf(s[4 * q4 + 2], s[4 * q4 + 3]));
-        float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        mx = max_halves(mx);
-        rescale(h, fmaxf(m_run[h], mx * c));           // -inf stays -inf (c > 0)
-    };
-    // P = exp2(S*c - m) as 16-bit B operands; masked scores are -inf -> 0
-    auto softmax_exp = [&](int h) __attribute__((always_inline)) {
+
+    // ---- softmax of one tile ------------------------------------------------
+    // The running max m is lazy: a row's weights are exp2(S c - m) with the
+    // stale m as long as none exceeds 2^8 (threshold 8 in log2 units).  A
+    // tile is first exponentiated with the stale max; when some lane's sum of
+    // weights exceeds 2^8 (only then can one weight exceed 2^8) or a row has
+    // no max yet, the rare path takes the true row max, raises m (rescaling
+    // O and l) where it exceeds m by more than the threshold, and
+    // exponentiates the tile again.  The result equals raising m whenever a
+    // tile max exceeds it by more than the threshold.
+    // Two normalisers: O is divided by the sum of the 16-bit weights
+    // actually fed to P.V (so its weights sum to one: a row dominated by one
+    // key reproduces that key's V row), LSE by the sum of the fp32 values
+    // (16-bit rounding would bias it by up to 2^-9).  Both are summed as
+    // trees: with one wave per SIMD a chain of dependent adds stalls.
+    auto exps_plain = [&](int h) __attribute__((always_inline)) {
         const float m_use = m_run[h] == -INFINITY ? 0.f : m_run[h];
-        float x[16];
+        float x[16], r2[2] = {0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = exp2_fast(fmaf(sacc[h][e], c, -m_use));
-        // two normalisers: O is divided by the sum of the 16-bit weights
-        // actually fed to P.V (so its weights sum to one); LSE uses the sum
-        // of the fp32 values (16-bit rounding would bias it by up to 2^-9).
-        // Both are summed as trees: with one wave per SIMD a serial chain of
-        // dependent adds would stall the wave.
-        float lr2[2] = {0.f, 0.f};
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
-            // element e is slot (e & 7) of reduction step e >> 3
             pb[h][e >> 3][(e & 7) >> 1] = pk;
-            lr2[(e >> 1) & 1] = dot2_ones<BF16>(pk, lr2[(e >> 1) & 1]);
+            r2[(e >> 1) & 1] = dot2_ones<BF16>(pk, r2[(e >> 1) & 1]);
         }
 #pragma unroll
         for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
             for (int e = 0; e < w; ++e) x[e] += x[e + w];
-        l_run[h] += x[0];
-        lr_run[h] += lr2[0] + lr2[1];
+        return f32x2{x[0], r2[0] + r2[1]};
     };
-    auto pv = [&](int h) __attribute__((always_inline)) {
+    auto refresh = [&](int h) __attribute__((always_inline)) {
+        asm volatile("");   // keep this rare block a real branch (not speculated)
+        f32x16& s = sacc[h];
+        float m4[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            m4[q4] = fmaxf(fmaxf(s[4 * q4], s[4 * q4 + 1]), fmaxf(s[4 * q4 + 2], s[4 * q4 + 3]));
+        const float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+        const float mnew = fmaxf(m_run[h], mx * c);          // -inf stays -inf (c > 0)
+        const bool raise = mnew > m_run[h] + kRescaleThreshold;
+        const float alpha = raise ? exp2_fast(m_run[h] - mnew) : 1.f;
+        l_run[h] *= alpha;
+        lr_run[h] *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[h][db][e] *= alpha;
+        m_run[h] = raise ? mnew : m_run[h];
+        return exps_plain(h);
+    };
+    // sums: (fp32, 16-bit) of this lane's weights of the tile
+    auto settle = [&](int h, f32x2 sums, bool first) __attribute__((always_inline)) {
+        if ((__builtin_amdgcn_ballot_w64(first) | __builtin_amdgcn_ballot_w64(sums.x > 256.f)) != 0ull)
+            sums = refresh(h);
+        l_run[h] += sums.x;
+        lr_run[h] += sums.y;
+    };
+    auto softmax_tile = [&](int h) __attribute__((always_inline)) {
+        const bool first = m_run[h] == -INFINITY;
+        settle(h, exps_plain(h), first);
+    };
+    // invisible scores of half h's tile jt -> -inf
+    auto apply_mask = [&](int h, int jt) __attribute__((always_inline)) {
+        const int lo = rel_lo[h] - jt * T::BN, hi = rel_hi[h] - jt * T::BN;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int off = 8 * (e >> 2) + (e & 3);
+            sacc[h][e] = (off >= lo && off <= hi) ? sacc[h][e] : -INFINITY;
+        }
+    };
+    auto qk = [&](int h, const u32x4 (&kq)[T::KS]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[h][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) sacc[h] = mfma32x32x16<BF16>(kq[ks], qreg[h][ks], sacc[h]);
+    };
+    auto pv = [&](int h, const u32x4 (&vq)[T::KK][T::DB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < T::KK; ++kk)
 #pragma unroll
             for (int db = 0; db < T::DB; ++db)
-                oacc[h][db] = mfma32x32x16<BF16>(vreg[kk][db], pb[h][kk], oacc[h][db]);
+                oacc[h][db] = mfma32x32x16<BF16>(vq[kk][db], pb[h][kk], oacc[h][db]);
     };
 
-    // One half-step of the unmasked body in a fixed instruction order: the
-    // S MFMAs of half hs interleaved with the exponentials of half hp, then
-    // half hp's P.V MFMAs interleaved with its sums and half hs's row max.
-    // With one wave per SIMD the matrix and vector pipes only overlap as far
-    // as the instruction stream alternates them, so sched_barrier(0) fences
-    // keep this order.
-    auto region = [&](int hs, int hp) __attribute__((always_inline)) {
-        constexpr int EPK = 16 / T::KS;                 // exponentials per S MFMA
-        const float m_use = m_run[hp] == -INFINITY ? 0.f : m_run[hp];
-        float x[16];
+    // One region of an unmasked step in a fixed instruction order.  Its
+    // slots are the S MFMAs of half hs (new tile), then the P.V MFMAs of
+    // half hs (previous tile, P from the region before); beside them the
+    // exponentials of the other half hp (its S from the region before) are
+    // spread evenly, with their packing and sums, and load(i) issues the
+    // operand loads of slot i.  Nothing in a region waits for a result of
+    // the same region.  sched_barrier(0) fences keep the order: with one
+    // wave per SIMD the matrix and vector pipes only overlap as far as the
+    // instruction stream alternates them.
+    auto fast_region = [&](auto hsc, const u32x4 (&kq)[T::KS], const u32x4 (&vq)[T::KK][T::DB],
+                           auto&& load) __attribute__((always_inline)) {
+        constexpr int hs = decltype(hsc)::value, hp = 1 - hs;
+        constexpr int NS = T::KS + T::KK * T::DB;       // MFMA slots
+        constexpr int EPS = 16 / NS;                    // exponentials per slot
+        static_assert(EPS * NS == 16, "whole exponentials per slot");
+        const bool first = m_run[hp] == -INFINITY;
+        const float m_use = first ? 0.f : m_run[hp];
+        float x[16], a[8], bsum[4], r2[2] = {0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[hs][e] = 0.f;
+        for (int i = 0; i < NS; ++i) {
+            if (i < T::KS) {
+                sacc[hs] = mfma32x32x16<BF16>(kq[i], qreg[hs][i], i == 0 ? f32x16{} : sacc[hs]);
+            } else {
+                const int kk = (i - T::KS) / T::DB, db = (i - T::KS) % T::DB;
+                oacc[hs][db] = mfma32x32x16<BF16>(vq[kk][db], pb[hs][kk], oacc[hs][db]);
+            }
+            load(i);
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) {
-            sacc[hs] = mfma32x32x16<BF16>(kreg[ks], qreg[hs][ks], sacc[hs]);
-#pragma unroll
-            for (int j = 0; j < EPK; ++j) {
-                const int e = ks * EPK + j;
+            for (int j = 0; j < EPS; ++j) {
+                const int e = i * EPS + j;
                 x[e] = exp2_fast(fmaf(sacc[hp][e], c, -m_use));
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+            // pair j (elements 2j, 2j+1) is packed and summed in the slot
+            // after its second exponential; pairs of sums one slot later
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) pb[hp][e >> 3][(e & 7) >> 1] = pack2<BF16>(x[e], x[e + 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        // P.V of half hp; beside it: 8 v_dot2 (16-bit sum), 15 adds (fp32
-        // sum tree), then half hs's row max once its S MFMAs have drained
-        float lr2[2] = {0.f, 0.f};
-        float m4[4];
-        float mx = 0.f;
-#pragma unroll
-        for (int i = 0; i < T::KK * T::DB; ++i) {
-            const int kk = i / T::DB, db = i % T::DB;
-            oacc[hp][db] = mfma32x32x16<BF16>(vreg[kk][db], pb[hp][kk], oacc[hp][db]);
-            // (the sums are pinned to their slot: left alone the compiler
-            // sinks them to their next use, outside this interleave)
-            if (i == 0) {
-#pragma unroll
-                for (int u = 0; u < 4; ++u) lr2[u & 1] = dot2_ones<BF16>(pb[hp][u >> 2][u & 3], lr2[u & 1]);
-                pin(lr2[0]); pin(lr2[1]);
-            } else if (i == 1) {
-#pragma unroll
-                for (int u = 4; u < 8; ++u) lr2[u & 1] = dot2_ones<BF16>(pb[hp][u >> 2][u & 3], lr2[u & 1]);
-                lr_run[hp] += lr2[0] + lr2[1];
-                pin(lr_run[hp]);
-            } else if (i == 2) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] += x[e + 8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pin(x[e]);
-            } else if (i == 3) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] += x[e + 4];
-                x[0] += x[2]; x[1] += x[3];
-                l_run[hp] += x[0] + x[1];
-                pin(l_run[hp]);
-            } else if (i == T::KK * T::DB - 3) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-                    m4[q4] = fmaxf(fmaxf(sacc[hs][4 * q4], sacc[hs][4 * q4 + 1]),
-                                   fmaxf(sacc[hs][4 * q4 + 2], sacc[hs][4 * q4 + 3]));
-            } else if (i == T::KK * T::DB - 2) {
-                mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            for (int j = 0; j < 8; ++j) {
+                if ((2 * j + 1) / EPS + 1 == i) {
+                    pb[hp][j >> 2][j & 3] = pack2<BF16>(x[2 * j], x[2 * j + 1]);
+                    pin_u(pb[hp][j >> 2][j & 3]);   // (else sunk past the rare-path branch)
+                    a[j] = x[2 * j] + x[2 * j + 1];
+                }
+                if ((2 * j + 1) / EPS + 2 == i) {
+                    r2[j & 1] = dot2_ones<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
+                    pin(r2[j & 1]);
+                    if (j & 1) bsum[j >> 1] = a[j - 1] + a[j];
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        rescale(hs, fmaxf(m_run[hs], mx * c));
-    };
-    auto body_fast = [&](int jt) __attribute__((always_inline)) {
-        load_k(kslot(jt));
-        region(0, 1);
-        load_v(vslot(jt));
-        region(1, 0);
+        // pairs not yet done
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if ((2 * j + 1) / EPS + 1 >= NS) {
+                pb[hp][j >> 2][j & 3] = pack2<BF16>(x[2 * j], x[2 * j + 1]);
+                pin_u(pb[hp][j >> 2][j & 3]);
+                a[j] = x[2 * j] + x[2 * j + 1];
+            }
+            if ((2 * j + 1) / EPS + 2 >= NS) {
+                r2[j & 1] = dot2_ones<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
+                if (j & 1) bsum[j >> 1] = a[j - 1] + a[j];
+            }
+        }
+        settle(hp, f32x2{(bsum[0] + bsum[1]) + (bsum[2] + bsum[3]), r2[0] + r2[1]}, first);
     };
 
-    // Step with new tile jt (see the pipeline above).  On entry half B's
-    // scores of tile jt-1 carry their final row max and V_{jt-1} is in vreg.
-    auto body = [&](int jt, bool masked) __attribute__((always_inline)) {
-        load_k(kslot(jt));
-        qk(0);
-        softmax_exp(1);
-        pv(1);
-        rowmax(0, jt, masked);
-        qk(1);
-        softmax_exp(0);
-        load_v(vslot(jt));
-        pv(0);
-        rowmax(1, jt, masked);
-    };
-    // A step with new tile jt: copies (even steps), the body, the barrier
-    // (odd steps).  Steps that need a mask (or compute nothing) run in the
-    // loops before and after the unmasked run, so the unmasked loop body is
-    // straight-line code.
-    auto step = [&](int jt, bool even, bool fast) __attribute__((always_inline)) {
-        if (even) {
-            issue(jt + T::STAGES - 2);
-            issue(jt + T::STAGES - 1);
-        }
-        if (fast)
-            body_fast(jt);
-        else if (jt >= act_lo && jt <= act_hi)
-            body(jt, true);
+    // An unmasked step with new tile jt and static parity P.  On entry K_jt
+    // is in kbuf[P] and V_{jt-1} in vbuf[1-P]; the step loads K_{jt+1} and
+    // V_jt into the other two buffers (the loads are issued one per slot and
+    // claimed at the end of the step, so no slot waits for LDS).
+    auto fast_step = [&](auto pc, int jt, bool even) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        // this step's set copies go out one every few slots: issued all at
+        // once by the four waves of a CU they queue at its address unit
+        const SetCopy sc = set_copy(jt + T::STAGES - 2);
+        constexpr int CSTEP = (T::KS + T::KK * T::DB) / T::LPS;
+        const uint16_t* kt = kslot(jt + 1);
+        const uint16_t* vt = vslot(jt);
+        constexpr int NQ = T::KK * T::DB;
+        u32x4 kn[T::KS];
+        u32x2 vlo[NQ], vhi[NQ];
+        fast_region(int_c<0>{}, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
+            if (i < T::KS) kn[i] = k_load(kt, i);
+            else vlo[i - T::KS] = v_half(vt, i - T::KS, 0);
+            if (i % CSTEP == CSTEP / 2) copy_one(sc, i / CSTEP);
+        });
+        fast_region(int_c<1>{}, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
+            if (i < NQ) vhi[i] = v_half(vt, i, 1);
+        });
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) kbuf[1 - P][ks] = in_acc_regs(kn[ks]);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            vbuf[P][q / T::DB][q % T::DB] =
+                in_acc_regs((u32x4){vlo[q].x, vlo[q].y, vhi[q].x, vhi[q].y});
         if (!even) sync_pair();
     };
 
-    // before the first computed step half B has no previous tile: scores
-    // -inf give P = 0, and zero V keeps 0 * V exact
+    // A step with new tile jt that needs masks (or computes nothing): same
+    // pipeline, generic instruction order, operands loaded when needed (K_jt
+    // into kbuf[0] first, V_jt into vbuf[1] once V_{jt-1} is done).
+    auto step_masked = [&](int jt, bool even) __attribute__((always_inline)) {
+        issue(jt + T::STAGES - 2);
+        if (jt >= act_lo && jt <= act_hi) {
+            load_k_now(kslot(jt));
+            qk(0, kbuf[0]);
+            softmax_tile(1);
+            pv(0, vbuf[1]);
+            apply_mask(0, jt);
+            qk(1, kbuf[0]);
+            softmax_tile(0);
+            pv(1, vbuf[1]);
+            apply_mask(1, jt);
+            load_v_now(vslot(jt));
+        }
+        if (!even) sync_pair();
+    };
+
+    // Pipeline: step jt computes S_A(jt), S_B(jt) = K_jt Q^T; P_B(jt-1) and
+    // P_A(jt); O_A and O_B += V_{jt-1} P(jt-1).  Before the first computed
+    // step there is no previous tile: S_B = -inf gives P_B = 0, and P_A = 0
+    // with V = 0 keeps 0 * V exact.  The step after the last tile only
+    // finishes the previous one.
 #pragma unroll
     for (int e = 0; e < 16; ++e) sacc[1][e] = -INFINITY;
 #pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kk = 0; kk < T::KK; ++kk) pb[h][kk] = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
     for (int kk = 0; kk < T::KK; ++kk)
 #pragma unroll
-        for (int db = 0; db < T::DB; ++db) vreg[kk][db] = (u32x4){0u, 0u, 0u, 0u};
+        for (int db = 0; db < T::DB; ++db) vbuf[1][kk][db] = (u32x4){0u, 0u, 0u, 0u};
 
     if (ntiles > 0) {
-        // sets 0 .. STAGES-3; the first pair of steps reads sets 0 and 1
+        // sets 0 .. STAGES-3; the first pair of steps reads sets 0 .. 2
         for (int s = tile_lo; s < tile_lo + T::STAGES - 2; ++s) issue(s);
         sync_pair();
-        // steps r = 0 .. ntiles (new tile tile_lo + r; the last one only
-        // finishes half B); the unmasked ones [rf_lo, rf_hi] run two per
-        // iteration (static parity), starting at an even step
+        // steps r = 0 .. ntiles (new tile tile_lo + r); the unmasked ones
+        // [rf_lo, rf_hi] run two per iteration (static parity), starting at
+        // an even step
         const int rf_lo = max(fast_lo - tile_lo, 0), rf_hi = fast_hi - tile_lo;
         int r = 0;
-        for (; r < rf_lo || (r <= rf_hi && (r & 1)); ++r) step(tile_lo + r, (r & 1) == 0, false);
-        for (; r + 1 <= rf_hi; r += 2) {
-            step(tile_lo + r, true, true);
-            step(tile_lo + r + 1, false, true);
+        for (; r < rf_lo || (r <= rf_hi && (r & 1)); ++r) step_masked(tile_lo + r, (r & 1) == 0);
+        if (r + 1 <= rf_hi) {
+            load_k_now(kslot(tile_lo + r));
+            for (; r + 1 <= rf_hi; r += 2) {
+                fast_step(int_c<0>{}, tile_lo + r, true);
+                fast_step(int_c<1>{}, tile_lo + r + 1, false);
+            }
         }
-        for (; r <= ntiles; ++r) step(tile_lo + r, (r & 1) == 0, false);
+        for (; r <= ntiles; ++r) step_masked(tile_lo + r, (r & 1) == 0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // DMA loads of unused sets still in flight
 
