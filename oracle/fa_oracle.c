@@ -232,3 +232,96 @@ int fa_oracle_decode(const double* q, const double* kc, const double* vc,
     }
     return err;
 }
+
+/* Gradients of the padded-batch attention (the training backward).
+ *
+ * The "FlashAttention" explainer page, "Step 5" and "Backward pass in a bit
+ * more detail": the backward needs the gradients with respect to the
+ * queries, keys and values; the fused kernel rebuilds the weights from
+ * recomputed scores and the saved row statistic.  What those gradients are
+ * is fixed by the forward definition alone (O = softmax(S) V with
+ * S = scale * Q K^T over the visible keys); this function writes out the
+ * chain rule of that definition for one row i, with P the row's softmax
+ * weights and dO the incoming gradient of the row's output:
+ *     dV_j += P_j dO_i                    dP_j = dO_i . V_j
+ *     D_i   = sum_j P_j dP_j              dS_j = P_j (dP_j - D_i)
+ *     dQ_i  = scale sum_j dS_j K_j        dK_j += scale dS_j Q_i
+ * over visible keys j; dK and dV of a K/V head collect every query head of
+ * its group (grouped-query attention).  A row with no visible key
+ * contributes nothing and gets dQ_i = 0.  The weights are recomputed here
+ * from the scores (two passes: max, then exp and sum), not read from a
+ * saved LSE.
+ *
+ * q, dout, dq: [B,Sq,Hq,d]; k, v, dk, dv: [B,Sk,Hkv,d].  Parallel over
+ * (sequence, K/V head) pairs, so each thread owns the dK/dV rows it adds to
+ * and every sum runs in a fixed order. */
+int fa_oracle_bwd(const double* q, const double* k, const double* v, const double* dout,
+                  double* dq, double* dk, double* dv,
+                  int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                  int causal, int wl, int wr, double scale)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return -2;
+    int G = Hq / Hkv;
+    long kvs = (long)Hkv * d;   /* token stride of k, v, dk, dv */
+    long qs = (long)Hq * d;     /* token stride of q, dout, dq */
+    for (long t = 0; t < (long)B * Sk * Hkv * d; ++t) { dk[t] = 0.0; dv[t] = 0.0; }
+    int err = 0;
+#pragma omp parallel
+    {
+        size_t n = (size_t)(Sk > 0 ? Sk : 1);
+        double* p = (double*)malloc(sizeof(double) * n);
+        double* dp = (double*)malloc(sizeof(double) * n);
+        if (!p || !dp) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic, 1)
+            for (int b = 0; b < B; ++b)
+                for (int g = 0; g < Hkv; ++g) {
+                    const double* kb = k + ((long)b * Sk * Hkv + g) * d;
+                    const double* vb = v + ((long)b * Sk * Hkv + g) * d;
+                    double* dkb = dk + ((long)b * Sk * Hkv + g) * d;
+                    double* dvb = dv + ((long)b * Sk * Hkv + g) * d;
+                    for (int h = g * G; h < (g + 1) * G; ++h)
+                        for (long i = 0; i < Sq; ++i) {
+                            const double* qrow = q + ((long)b * Sq + i) * qs + (long)h * d;
+                            const double* gorow = dout + ((long)b * Sq + i) * qs + (long)h * d;
+                            double* dqrow = dq + ((long)b * Sq + i) * qs + (long)h * d;
+                            for (int c = 0; c < d; ++c) dqrow[c] = 0.0;
+                            double m = -INFINITY;
+                            for (long j = 0; j < Sk; ++j) {
+                                if (!visible(i, j, Sq, Sk, causal, wl, wr)) continue;
+                                p[j] = scale * dot(qrow, kb + j * kvs, d);
+                                if (p[j] > m) m = p[j];
+                            }
+                            if (m == -INFINITY) continue;   /* no visible key */
+                            double l = 0.0;
+                            for (long j = 0; j < Sk; ++j)
+                                if (visible(i, j, Sq, Sk, causal, wl, wr)) l += exp(p[j] - m);
+                            double D = 0.0;
+                            for (long j = 0; j < Sk; ++j) {
+                                if (!visible(i, j, Sq, Sk, causal, wl, wr)) continue;
+                                p[j] = exp(p[j] - m) / l;
+                                dp[j] = dot(gorow, vb + j * kvs, d);
+                                D += p[j] * dp[j];
+                            }
+                            for (long j = 0; j < Sk; ++j) {
+                                if (!visible(i, j, Sq, Sk, causal, wl, wr)) continue;
+                                const double ds = p[j] * (dp[j] - D);
+                                const double* krow = kb + j * kvs;
+                                double* dkrow = dkb + j * kvs;
+                                double* dvrow = dvb + j * kvs;
+                                for (int c = 0; c < d; ++c) {
+                                    dqrow[c] += scale * ds * krow[c];
+                                    dkrow[c] += scale * ds * qrow[c];
+                                    dvrow[c] += p[j] * gorow[c];
+                                }
+                            }
+                        }
+                }
+        }
+        free(p);
+        free(dp);
+    }
+    return err;
+}

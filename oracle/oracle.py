@@ -49,8 +49,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                      i32, i32, i32, f64]
     lib.fa_oracle_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                      i32, i32, i32, f64]
+    lib.fa_oracle_bwd.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                  i32, i32, i32, f64]
     for f in (lib.fa_oracle_rows, lib.fa_oracle_fwd, lib.fa_oracle_varlen,
-              lib.fa_oracle_decode):
+              lib.fa_oracle_decode, lib.fa_oracle_bwd):
         f.restype = ctypes.c_int
     return lib
 
@@ -121,6 +123,24 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"oracle fwd failed: {rc}")
         return out, lse
+
+    # -- gradients (padded batch) -------------------------------------------
+    def attention_bwd(self, q, k, v, dout, causal=False, window=(-1, -1), scale=None):
+        """q, dout: [B,Sq,Hq,d]; k,v: [B,Sk,Hkv,d] -> (dq, dk, dv) of the
+        padded-batch attention for the incoming output gradient dout."""
+        q, k, v, go = _f64(q), _f64(k), _f64(v), _f64(dout)
+        B, Sq, Hq, d = q.shape
+        Bk, Sk, Hkv, dk_ = k.shape
+        assert Bk == B and dk_ == d and v.shape == k.shape and go.shape == q.shape
+        dq = np.empty_like(q)
+        dk = np.empty_like(k)
+        dv = np.empty_like(v)
+        rc = self.lib.fa_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(go), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), B, Hq, Hkv, Sq, Sk, d, int(bool(causal)),
+                                    int(window[0]), int(window[1]), _scale(scale, d))
+        if rc != 0:
+            raise RuntimeError(f"oracle bwd failed: {rc}")
+        return dq, dk, dv
 
     # -- packed sequences --------------------------------------------------
     def attention_varlen(self, q, k, v, cu_q, cu_k, causal=False, window=(-1, -1),
@@ -205,6 +225,10 @@ def attention_varlen(*a, **kw):
 
 def attention_decode(*a, **kw):
     return default().attention_decode(*a, **kw)
+
+
+def attention_bwd(*a, **kw):
+    return default().attention_bwd(*a, **kw)
 
 
 def attention_rows(*a, **kw):

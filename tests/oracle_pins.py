@@ -14,7 +14,10 @@ AssertionError when the oracle disagrees with
     permutation, GQA equals MHA with repeated K/V heads, packed equals
     per-sequence, decode equals the last prefill row, key translation,
     split-and-combine by LSE);
-  * a 30-digit mpmath brute force on tiny inputs.
+  * a 30-digit mpmath brute force on tiny inputs;
+  * for the gradients: central finite differences through the forward
+    oracle, torch float64 autograd of an explicit masked softmax, and exact
+    identities (row weights sum to one, key-translation invariance).
 
 The functions are shared by ``test_oracle_pins.py`` (the real oracle) and
 ``test_oracle_mutations.py`` (deliberately broken copies of the oracle, each
@@ -433,10 +436,122 @@ def pin_mpmath_brute_force(orc):
                     assert abs(float(o) - out[0, i, h, t]) < 1e-12
 
 
+# ---------------------------------------------------------------------------
+# Gradients (fa_oracle_bwd).  The pages fix only what the backward computes
+# (the gradients of the forward definition); these pins tie the oracle's
+# chain rule to the forward oracle (finite differences), to torch autograd,
+# and to exact identities of softmax attention.
+
+_BWD_CASES = [(4, 4, False, -1, -1), (4, 4, True, -1, -1), (3, 6, True, -1, -1),
+              (6, 6, True, 2, 0), (5, 5, False, 1, 2), (6, 3, True, -1, -1)]
+
+
+def pin_bwd_finite_differences(orc):
+    """dq, dk, dv equal central differences of L = sum(dout * O) through the
+    forward oracle, element by element (GQA, every mask mode, rows with no
+    visible key)."""
+    rng = _rng(40)
+    B, Hq, Hkv, d, scale, h = 1, 2, 1, 3, 0.83, 1e-6
+    for (Sq, Sk, causal, wl, wr) in _BWD_CASES:
+        q = _rand(rng, B, Sq, Hq, d); k = _rand(rng, B, Sk, Hkv, d); v = _rand(rng, B, Sk, Hkv, d)
+        go = _rand(rng, B, Sq, Hq, d)
+        dq, dk, dv = orc.attention_bwd(q, k, v, go, causal=causal, window=(wl, wr), scale=scale)
+
+        def loss(qq, kk, vv):
+            o, _ = orc.attention(qq, kk, vv, causal=causal, window=(wl, wr), scale=scale)
+            return float((o * go).sum())
+
+        for x, gx, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp = x.copy(); xp[idx] += h
+                xm = x.copy(); xm[idx] -= h
+                args_p = [q, k, v]; args_p[which] = xp
+                args_m = [q, k, v]; args_m[which] = xm
+                num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert np.abs(num - gx).max() < 1e-7 * max(1.0, np.abs(gx).max()), (Sq, Sk, causal, which)
+
+
+def _torch_grads(q, k, v, go, causal, wl, wr, scale):
+    """float64 autograd through an explicit masked softmax (GQA by repeating
+    K/V heads, rows with no visible key give zero weights)."""
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3).clone().requires_grad_(True)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).clone().requires_grad_(True)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).clone().requires_grad_(True)
+    G = tq.shape[1] // tk.shape[1]
+    kk = tk.repeat_interleave(G, dim=1)
+    vv = tv.repeat_interleave(G, dim=1)
+    mask = _visible_band(q.shape[1], k.shape[1], causal, wl, wr)
+    s = (tq @ kk.transpose(-1, -2)) * scale
+    s = s.masked_fill(~mask, float("-inf"))
+    m = s.amax(-1, keepdim=True).clamp_min(-1e300)      # rows with no key: all -inf
+    e = torch.exp(s - m).masked_fill(~mask, 0.0)
+    z = e.sum(-1, keepdim=True)
+    p = e / torch.where(z > 0, z, torch.ones_like(z))
+    o = p @ vv
+    o.backward(torch.from_numpy(go).permute(0, 2, 1, 3))
+    return (tq.grad.permute(0, 2, 1, 3).numpy(), tk.grad.permute(0, 2, 1, 3).numpy(),
+            tv.grad.permute(0, 2, 1, 3).numpy())
+
+
+def pin_bwd_torch_autograd(orc):
+    """torch float64 autograd of the same attention (independent code path)."""
+    rng = _rng(41)
+    B, Hq, Hkv, d, scale = 2, 4, 2, 8, 0.35
+    for (Sq, Sk, causal, wl, wr) in _BWD_CASES + [(17, 23, True, 5, -1), (23, 17, False, -1, -1)]:
+        q = _rand(rng, B, Sq, Hq, d); k = _rand(rng, B, Sk, Hkv, d); v = _rand(rng, B, Sk, Hkv, d)
+        go = _rand(rng, B, Sq, Hq, d)
+        got = orc.attention_bwd(q, k, v, go, causal=causal, window=(wl, wr), scale=scale)
+        ref = _torch_grads(q, k, v, go, causal, wl, wr, scale)
+        for a, r in zip(got, ref):
+            assert np.abs(a - r).max() < 1e-12, (Sq, Sk, causal, wl, wr)
+
+
+def pin_bwd_identities(orc):
+    """Exact identities: the weights of a row sum to one, so sum_j dV_j =
+    sum of dout over rows with a visible key; adding one vector to every key
+    leaves O unchanged, so sum_j dK_j = 0; a key no row sees gets dK = dV = 0;
+    a row with no visible key gets dQ = 0."""
+    rng = _rng(42)
+    B, Hq, Hkv, d = 2, 4, 2, 5
+    for (Sq, Sk, causal, wl, wr) in _BWD_CASES:
+        q = _rand(rng, B, Sq, Hq, d); k = _rand(rng, B, Sk, Hkv, d); v = _rand(rng, B, Sk, Hkv, d)
+        go = _rand(rng, B, Sq, Hq, d)
+        dq, dk, dv = orc.attention_bwd(q, k, v, go, causal=causal, window=(wl, wr), scale=0.6)
+        vis = _visible_band(Sq, Sk, causal, wl, wr).numpy()
+        rows = vis.any(1)
+        G = Hq // Hkv
+        for g in range(Hkv):
+            want = go[:, rows][:, :, g * G:(g + 1) * G].sum(axis=(1, 2))
+            assert np.abs(dv[:, :, g].sum(1) - want).max() < 1e-12
+            assert np.abs(dk[:, :, g].sum(1)).max() < 1e-12
+        assert np.all(dq[:, ~rows] == 0)
+        cols = vis.any(0)
+        assert np.all(dk[:, ~cols] == 0) and np.all(dv[:, ~cols] == 0)
+
+
+def pin_bwd_gqa_equals_repeated_mha(orc):
+    """GQA gradients equal MHA gradients with K/V heads repeated, dK/dV summed
+    over each group."""
+    rng = _rng(43)
+    B, Sq, Sk, Hq, Hkv, d = 1, 7, 9, 6, 2, 4
+    q = _rand(rng, B, Sq, Hq, d); k = _rand(rng, B, Sk, Hkv, d); v = _rand(rng, B, Sk, Hkv, d)
+    go = _rand(rng, B, Sq, Hq, d)
+    G = Hq // Hkv
+    dq, dk, dv = orc.attention_bwd(q, k, v, go, causal=True, scale=0.5)
+    dq2, dk2, dv2 = orc.attention_bwd(q, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2), go,
+                                      causal=True, scale=0.5)
+    assert np.abs(dq - dq2).max() < 1e-12
+    assert np.abs(dk - dk2.reshape(B, Sk, Hkv, G, d).sum(3)).max() < 1e-12
+    assert np.abs(dv - dv2.reshape(B, Sk, Hkv, G, d).sum(3)).max() < 1e-12
+
+
 PINS = [
     pin_worked_example, pin_torch_sdpa, pin_zero_query_closed_form, pin_varlen_zero_query,
     pin_decode_zero_query, pin_constant_v, pin_single_visible_key, pin_one_hot_values,
     pin_masked_keys_no_effect, pin_key_permutation, pin_gqa_equals_repeated_mha,
     pin_varlen_equals_per_sequence, pin_decode_equals_last_prefill_row, pin_key_translation,
     pin_split_combine, pin_fully_masked_rows, pin_large_scores_stable, pin_mpmath_brute_force,
+    pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_identities,
+    pin_bwd_gqa_equals_repeated_mha,
 ]

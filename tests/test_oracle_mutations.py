@@ -28,8 +28,10 @@ MUTANTS = {
                             "const double* vrow = k + j * kv_stride;"),
     "gqa_modulo_mapping": ("int g = h / G;\n                        const double* qrow",
                            "int g = h % Hkv;\n                        const double* qrow"),
-    "kv_head_ignored": ("const double* kb = k + ((long)b * Sk * Hkv + g) * d;",
-                        "const double* kb = k + ((long)b * Sk * Hkv) * d;"),
+    "kv_head_ignored": ("                        const double* kb = k + ((long)b * Sk * Hkv + g) * d;",
+                        "                        const double* kb = k + ((long)b * Sk * Hkv) * d;"),
+    "bwd_kv_head_ignored": ("for (int g = 0; g < Hkv; ++g) {\n                    const double* kb = k + ((long)b * Sk * Hkv + g) * d;",
+                            "for (int g = 0; g < Hkv; ++g) {\n                    const double* kb = k + ((long)b * Sk * Hkv) * d;"),
     "q_layout_bhsd": ("const double* qrow = q + (((long)b * Sq + i) * Hq + h) * d;",
                       "const double* qrow = q + (((long)b * Hq + h) * Sq + i) * d;"),
     "lse_layout_bsh": ("double* l = lse + ((long)b * Hq + h) * Sq + i;",
@@ -41,6 +43,15 @@ MUTANTS = {
     "decode_gqa_modulo": ("int g = h / G;\n                    const double* kb = kc",
                           "int g = h % Hkv;\n                    const double* kb = kc"),
     "max_not_tracked": ("if (scores[j] > m) m = scores[j];", "if (m == -INFINITY) m = scores[j];"),
+    "bwd_missing_row_term": ("const double ds = p[j] * (dp[j] - D);", "const double ds = p[j] * dp[j];"),
+    "bwd_sign_flipped": ("const double ds = p[j] * (dp[j] - D);", "const double ds = p[j] * (D - dp[j]);"),
+    "bwd_dq_without_scale": ("dqrow[c] += scale * ds * krow[c];", "dqrow[c] += ds * krow[c];"),
+    "bwd_dk_from_keys": ("dkrow[c] += scale * ds * qrow[c];", "dkrow[c] += scale * ds * krow[c];"),
+    "bwd_unnormalised_weights": ("p[j] = exp(p[j] - m) / l;", "p[j] = exp(p[j] - m);"),
+    "bwd_dp_from_keys": ("dp[j] = dot(gorow, vb + j * kvs, d);", "dp[j] = dot(gorow, kb + j * kvs, d);"),
+    "bwd_first_group_head_only": ("for (int h = g * G; h < (g + 1) * G; ++h)",
+                                  "for (int h = g * G; h < g * G + 1; ++h)"),
+    "bwd_dv_from_queries": ("dvrow[c] += p[j] * gorow[c];", "dvrow[c] += p[j] * qrow[c];"),
 }
 
 
