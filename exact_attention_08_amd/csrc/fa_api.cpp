@@ -202,6 +202,62 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
     return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
 }
 
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq) {
+    if (B < 1 || Hq < 1 || Sq < 1) return 0;
+    return (size_t)B * Hq * Sq * sizeof(float);
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+                   int Sk, int d, int causal, int window_left, int window_right,
+                   float softmax_scale, void* workspace, size_t workspace_bytes, fa_dtype_t dtype,
+                   hipStream_t stream) {
+    if (Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARG, "Sq, Sk must be >= 0 (got %d, %d)", Sq, Sk);
+    // tensors of a side with no rows may be NULL (an empty torch tensor has
+    // no storage); the shared checks then see stand-ins that pass them
+    alignas(16) static const uint64_t kNone[2] = {0, 0};
+    const void* const none = kNone;
+    fa_status_t st = check_common(Sq > 0 ? q : none, Sk > 0 ? k : none, Sk > 0 ? v : none,
+                                  Sq > 0 ? out : none, Sq > 0 ? lse : nullptr, B, Hq, Hkv, d,
+                                  window_left, window_right, softmax_scale, dtype);
+    if (st != FA_OK) return st;
+    if (Sq > 0 && (!dout || !aligned16(dout)))
+        return fail(FA_ERR_INVALID_ARG, "dout must be non-null and 16-byte aligned");
+    if (Sq > 0 && (!dq || !aligned16(dq)))
+        return fail(FA_ERR_INVALID_ARG, "dq must be non-null and 16-byte aligned");
+    if (Sk > 0 && (!dk || !dv || !aligned16(dk) || !aligned16(dv)))
+        return fail(FA_ERR_INVALID_ARG, "dk and dv must be non-null and 16-byte aligned");
+    if (Sq > 0 && !lse) return fail(FA_ERR_INVALID_ARG, "lse (the forward's) must be non-null");
+    if (Sq == 0 && Sk == 0) return ok();
+    if ((st = check_seq_bytes(Sq, Hq, d, "q")) != FA_OK) return st;
+    if ((st = check_seq_bytes(Sk, Hkv, d, "k/v")) != FA_OK) return st;
+    const size_t need = fa_bwd_workspace_bytes(B, Hq, Sq);
+    if (need > 0 && (!workspace || !aligned16(workspace)))
+        return fail(FA_ERR_WORKSPACE, "workspace must be non-null and 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    fa::BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = out; p.dout = dout; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.dsum = static_cast<float*>(workspace);
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sq = Sq; p.Sk = Sk;
+    p.q_tok_stride = (long long)Hq * d;
+    p.kv_tok_stride = (long long)Hkv * d;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    p.scale = softmax_scale;
+    p.c2 = softmax_scale * fa::kLog2e_host;
+    p.nkb = (Sk + fa::kBwdKeysPerWg - 1) / fa::kBwdKeysPerWg;
+    p.gw = fa::fwd_heads_per_wg(p.G);
+    const int bmq = 32 * fa::kBwdWaves / p.gw;
+    p.nqb = (Sq + bmq - 1) / bmq;
+    if ((long long)p.nkb * Hkv * B * fa::kBwdThreads > kMaxGridThreads ||
+        (long long)p.nqb * (Hq / p.gw) * B * fa::kBwdThreads > kMaxGridThreads ||
+        (long long)B * Sq * Hq * (d / 8) > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    return launch_status(fa::launch_bwd(p, d, dtype == FA_BF16, stream));
+}
+
 const char* fa_status_str(fa_status_t s) {
     switch (s) {
         case FA_OK: return "FA_OK";

@@ -51,9 +51,34 @@ struct DecodeParams {
     uint32_t qsign;
 };
 
+// Backward (gradients): row-term kernel, dK/dV kernel, dQ kernel.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;           // [B, Hq, Sq], natural log
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dsum;                // workspace [B, Hq, Sq]: D_i = dO_i . O_i
+    int B, Hq, Hkv, G;
+    int Sq, Sk;
+    long long q_tok_stride;     // Hq * d
+    long long kv_tok_stride;    // Hkv * d
+    int causal, wl, wr;
+    float scale;                // softmax scale (any sign)
+    float c2;                   // scale * log2(e)
+    int nkb;                    // 128-key blocks per (sequence, K/V head)
+    int gw;                     // query heads per dQ work-group
+    int nqb;                    // query blocks of 128/gw rows per (sequence, head group)
+};
+
 // Host launchers (defined next to their kernels).
 hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
+hipError_t launch_bwd(const BwdParams& p, int d, bool bf16, hipStream_t s);
 
 // Kernel tile geometry, shared with the host for grid sizing.
 constexpr int kFwdWaveRows = 64;   // query rows per forward wave
@@ -67,5 +92,8 @@ inline int fwd_rows_per_wg(int G) { return kFwdWaveRows * kFwdWaves / fwd_heads_
 constexpr int kDecodeWaves = 4;    // waves per decode split work-group
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr float kLog2e_host = 1.4426950408889634f;
+constexpr int kBwdWaves = 4;       // waves per backward work-group
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdKeysPerWg = 32 * kBwdWaves;   // dK/dV work-group: 32 keys per wave
 
 }  // namespace fa

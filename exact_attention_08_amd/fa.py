@@ -24,7 +24,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_E
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
-           "fa_status_str", "fa_last_error")
+           "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str", "fa_last_error")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +59,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_decode_kvcache.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
                                           ctypes.c_size_t, I, P]
         lib.fa_decode_kvcache.restype = I
+        lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
+        lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P,
+                               ctypes.c_size_t, I, P]
+        lib.fa_bwd.restype = I
         lib.fa_status_str.argtypes = [I]
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_last_error.argtypes = []
@@ -173,3 +178,33 @@ def decode_kvcache(q, k_cache, v_cache, cache_seqlens, max_seqlen_k, *, causal=F
                                  workspace.numel() * workspace.element_size(),
                                  _DTYPE[q.dtype], _stream()))
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, Hq: int, Sq: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, Hq, Sq))
+
+
+def bwd(q, k, v, out, dout, lse, *, causal=False, window=(-1, -1), softmax_scale=None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of the padded-batch attention: q, out, dout [B,Sq,Hq,d], k/v [B,Sk,Hkv,d],
+    lse [B,Hq,Sq] fp32 from fwd() -> (dq, dk, dv).  The fp32 workspace is allocated with
+    torch unless given (uint8 tensor of at least bwd_workspace_bytes)."""
+    _check_tensors(q, k, v, out, dout)
+    _require(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "expected 4-d q, k, v")
+    _require(out.shape == q.shape and dout.shape == q.shape, "out and dout must match q")
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    _require(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+             and tuple(lse.shape) == (B, Hq, Sq), "lse must be a contiguous fp32 [B,Hq,Sq] GPU tensor")
+    lib = load()
+    need = int(lib.fa_bwd_workspace_bytes(B, Hq, Sq))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check(lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                      _ptr(dk), _ptr(dv), B, Hq, Hkv, Sq, Sk, d, int(bool(causal)),
+                      int(window[0]), int(window[1]), _scale(softmax_scale, d), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _DTYPE[q.dtype], _stream()))
+    return dq, dk, dv

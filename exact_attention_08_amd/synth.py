@@ -82,6 +82,12 @@ def gen_padded(seed: int, B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int,
     return q, k, v
 
 
+def gen_grad(seed: int, shape, dtype: str = "bf16", sigma: float = 1.0) -> torch.Tensor:
+    """A seeded incoming gradient (dL/dO) of the given shape, N(0, sigma^2)."""
+    gen = torch.Generator().manual_seed(seed)
+    return _normal(gen, tuple(shape), sigma, DTYPES[dtype])
+
+
 def gen_lengths(gen: torch.Generator, n: int, lo: int, hi: int) -> torch.Tensor:
     """n integer lengths uniform in [lo, hi] (inclusive)."""
     return torch.randint(lo, hi + 1, (n,), generator=gen, dtype=torch.int64)

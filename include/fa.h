@@ -1,6 +1,7 @@
 /*
- * fa.h -- C ABI of the fused exact-attention forward library for MI355X
- * (gfx950).  Link against libfa355.so.
+ * fa.h -- C ABI of the fused exact-attention library for MI355X (gfx950):
+ * forward, KV-cache decode and the training backward.  Link against
+ * libfa355.so.
  *
  * What is computed (all entry points): exact scaled-dot-product attention
  *     O = softmax(scale * Q K^T + mask) V,   LSE = log of the softmax normaliser,
@@ -134,6 +135,34 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
                               float softmax_scale, int split_size,
                               void* workspace, size_t workspace_bytes,
                               fa_dtype_t dtype, hipStream_t stream);
+
+/* Bytes of fp32 workspace fa_bwd needs: one value per query row and head
+ * (D_i = dO_i . O_i). */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq);
+
+/* Gradients of the padded-batch attention (the training backward): given
+ * the forward's inputs, its output `out` and LSE, and the gradient `dout` of
+ * a loss with respect to `out`, writes dq, dk, dv.  The score tiles are
+ * recomputed from q and k and the weights rebuilt from the saved LSE; no
+ * score matrix reaches memory ("FlashAttention" explainer page, "Step 5"
+ * and "Backward pass in a bit more detail").  dK and dV of a K/V head
+ * collect every query head of its group.
+ *   q, out, dout, dq : [B, Sq, Hq, d]      k, v, dk, dv : [B, Sk, Hkv, d]
+ *   lse              : [B, Hq, Sq] fp32, as written by fa_fwd for the same
+ *                      arguments (rows with no visible key: -inf)
+ *   workspace        : DEVICE scratch of at least fa_bwd_workspace_bytes(B,
+ *                      Hq, Sq) bytes, owned by the caller, contents ignored
+ *   other arguments as for fa_fwd.  Sq == 0 sets dk and dv to zero; Sk == 0
+ *   sets dq to zero (k, v, dk, dv may then be NULL).  Keys no row sees get
+ *   dk = dv = 0; rows with no visible key get dq = 0.
+ * Three kernels are enqueued on `stream`; none accumulates with atomics, so
+ * repeated calls give bitwise identical results. */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                   int causal, int window_left, int window_right, float softmax_scale,
+                   void* workspace, size_t workspace_bytes,
+                   fa_dtype_t dtype, hipStream_t stream);
 
 /* Static text of a status code. */
 const char* fa_status_str(fa_status_t s);

@@ -33,7 +33,8 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes",
-                                           "fa_decode_kvcache", "fa_status_str", "fa_last_error"])
+                                           "fa_decode_kvcache", "fa_bwd_workspace_bytes", "fa_bwd",
+                                           "fa_status_str", "fa_last_error"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -125,6 +126,34 @@ def test_workspace_exact_boundary(lib):
     need = lib.fa_decode_workspace_bytes(2, 8, 4096, 128, 1024)
     assert decode(lib, ws_bytes=need - 1) == 3
     assert "workspace too small" in lib.fa_last_error().decode()
+
+
+def bwd(lib, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=1 << 30, B=1,
+        Hq=4, Hkv=2, Sq=8, Sk=8, d=128, scale=0.125, dtype=0):
+    return lib.fa_bwd(FAKE, FAKE, FAKE, FAKE, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, d, 1, -1,
+                      -1, scale, ws, ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dout=None), 1), (dict(dout=MISALIGNED), 1), (dict(dq=None), 1), (dict(dk=None), 1),
+    (dict(dv=MISALIGNED), 1), (dict(lse=None), 1), (dict(ws=None), 3), (dict(ws=FAKE + 8), 3),
+    (dict(ws_bytes=4 * 8 * 4 - 1, B=1, Hq=4, Sq=8), 3), (dict(d=80), 2), (dict(dtype=5), 2),
+    (dict(Hq=6, Hkv=4), 1), (dict(scale=math.nan), 1), (dict(Sq=-2), 1),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.fa_bwd_workspace_bytes(4, 32, 4096) == 4 * 32 * 4096 * 4
+    assert lib.fa_bwd_workspace_bytes(0, 32, 4096) == 0
+
+
+def test_bwd_empty_is_a_noop(lib):
+    # no queries and no keys: nothing to write, nothing enqueued
+    assert bwd(lib, Sq=0, Sk=0, ws=None, ws_bytes=0) == 0
+    assert lib.fa_last_error().decode() == ""
 
 
 def test_status_strings(lib):

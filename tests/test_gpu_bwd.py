@@ -1,0 +1,162 @@
+"""GPU parity of the backward (fa_bwd through the C ABI) against the fp64
+oracle's gradients, element by element, on seeded inputs spanning several
+tiles with ragged tails, every mask mode, GQA, and the degenerate cases
+(rows that see no key, a single key, no keys, no queries).
+
+The GPU backward takes the GPU forward's own O and LSE, as a training step
+would; the oracle differentiates the exact definition.  Tolerance per element
+(``error_bounds``): 2^-8 times the sum of the absolute terms of the
+element's sum (16-bit P and dS operands), plus the effect of forming the row
+term D from the 16-bit forward output, plus 2^-8 |g| (output rounding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_08_amd import fa, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# name, B, Hq, Hkv, Sq, Sk, d, dtype, causal, window, scale, seed
+BWD_CASES = [
+    ("causal_gqa_ragged", 2, 8, 2, 300, 300, 128, "bf16", True, (-1, -1), None, 201),
+    ("noncausal_mha_fp16", 1, 4, 4, 200, 333, 128, "fp16", False, (-1, -1), None, 202),
+    ("noncausal_d64_ragged", 2, 4, 1, 130, 257, 64, "bf16", False, (-1, -1), None, 203),
+    ("causal_d64_fp16", 1, 6, 3, 384, 384, 64, "fp16", True, (-1, -1), None, 204),
+    ("causal_sq_lt_sk", 1, 4, 2, 77, 300, 128, "bf16", True, (-1, -1), None, 205),
+    ("causal_sq_gt_sk", 1, 4, 2, 300, 77, 128, "bf16", True, (-1, -1), None, 206),
+    ("window_causal", 1, 4, 4, 400, 400, 128, "fp16", True, (100, 100), None, 207),
+    ("window_two_sided", 1, 2, 1, 300, 300, 64, "bf16", False, (50, 30), None, 208),
+    ("window_right_only", 1, 2, 2, 260, 300, 128, "bf16", False, (-1, 40), None, 209),
+    ("negative_scale", 1, 2, 2, 150, 150, 128, "bf16", True, (-1, -1), -0.09, 210),
+    ("single_key", 1, 2, 2, 50, 1, 128, "bf16", False, (-1, -1), None, 211),
+    ("single_query", 2, 8, 2, 1, 300, 128, "bf16", True, (-1, -1), None, 212),
+    ("large_group", 1, 16, 1, 130, 130, 128, "bf16", True, (-1, -1), None, 213),
+    ("sigma_large_scores", 1, 4, 2, 256, 256, 128, "bf16", True, (-1, -1), 0.5, 214),
+    ("long_causal", 1, 4, 1, 1000, 1000, 128, "bf16", True, (-1, -1), None, 215),
+]
+
+
+def error_bounds(q, k, v, go, causal, window, scale):
+    """Per-element error bounds of the three gradients (tolerances only; the
+    expected values come from the oracle).
+
+    Each gradient element is a sum over rows or keys:
+        dV_jc = sum_i P_ij dO_ic,   dK_jc = scale sum_i dS_ij Q_ic,
+        dQ_ic = scale sum_j dS_ij K_jc,   dS_ij = P_ij (dP_ij - D_i),
+    and the kernels round P and dS to the input dtype before these products
+    (relative error <= 2^-9 per term; 2^-12 for fp16).  Under cancellation
+    the error is relative to the sum of the absolute terms A, not to the
+    result, so the bound is 2^-8 * A (a 2x margin), A summed here in fp64
+    with P, dP and dS written out per head.
+    The row term D_i = dO_i . O_i is formed from the forward's 16-bit output,
+    so each dS_ij of row i carries an error dD_i <= E_i =
+    2^-7 sum_c |dO_ic| (|O_ic| + 2^-7) (output rounding 2^-9 |O| plus the
+    forward's own error); it adds scale E_i |sum_j P_ij K_jc| to dQ and
+    scale sum_i P_ij E_i |Q_ic| to dK.  The final rounding of each gradient
+    to the input dtype adds 2^-8 |g| (in ``check``)."""
+    from oracle_pins import _visible_band
+    sc = scale if scale is not None else q.shape[-1] ** -0.5
+    qf, kf, vf, gf = (x.double().numpy() for x in (q, k, v, go))
+    B, Sq, Hq, d = qf.shape
+    Sk, Hkv = kf.shape[1], kf.shape[2]
+    G = Hq // Hkv
+    vis = _visible_band(Sq, Sk, causal, window[0], window[1]).numpy()
+    bq, bk, bv = np.zeros_like(qf), np.zeros_like(kf), np.zeros_like(vf)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = np.where(vis, sc * qf[b, :, h] @ kf[b, :, g].T, -np.inf)
+            m = s.max(1, keepdims=True)
+            m[~np.isfinite(m)] = 0.0
+            e = np.where(vis, np.exp(s - m), 0.0)
+            z = e.sum(1, keepdims=True)
+            P = e / np.where(z > 0, z, 1.0)
+            dO = gf[b, :, h]
+            O = P @ vf[b, :, g]
+            dP = dO @ vf[b, :, g].T
+            D = (dO * O).sum(1, keepdims=True)
+            aS = np.abs(P * (dP - D))
+            E = 2.0 ** -7 * (np.abs(dO) * (np.abs(O) + 2.0 ** -7)).sum(1, keepdims=True)
+            bv[b, :, g] += 2.0 ** -8 * (P.T @ np.abs(dO))
+            bk[b, :, g] += abs(sc) * (2.0 ** -8 * (aS.T @ np.abs(qf[b, :, h])) + P.T @ (E * np.abs(qf[b, :, h])))
+            bq[b, :, h] = abs(sc) * (2.0 ** -8 * (aS @ np.abs(kf[b, :, g])) + E * np.abs(P @ kf[b, :, g]))
+    return bq, bk, bv
+
+
+def check(name, got, ref, extra):
+    g = got.detach().to("cpu", torch.float64).numpy()
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    assert np.isfinite(g).all(), f"{name}: non-finite gradient"
+    err = np.abs(g - ref)
+    tol = 2.0 ** -8 * np.abs(ref) + extra
+    bad = err > tol
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    if ref.size:
+        w = int(np.argmax(err / np.maximum(tol, 1e-300)))
+        worst = float(err.reshape(-1)[w] / max(tol.reshape(-1)[w], 1e-300))
+        print(f"[grad] {name}: max|err| {err.max():.3e}  rms(ref) {rms:.3e}  worst err/tol "
+              f"{worst:.3f} at ref {ref.reshape(-1)[w]:.4e} got {g.reshape(-1)[w]:.4e} "
+              f"(index {np.unravel_index(w, ref.shape)})", flush=True)
+    assert not bad.any(), f"{name}: {int(bad.sum())} elements exceed the tolerance"
+
+
+def run_case(case):
+    name, B, Hq, Hkv, Sq, Sk, d, dt, causal, window, scale, seed = case
+    q, k, v = synth.gen_padded(seed, B, Hq, Hkv, Sq, Sk, d, dt)
+    go = synth.gen_grad(seed + 1000, q.shape, dt)
+    qd, kd, vd, god = q.to(DEV), k.to(DEV), v.to(DEV), go.to(DEV)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, window=window, softmax_scale=scale)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, god, lse, causal=causal, window=window,
+                        softmax_scale=scale)
+    torch.cuda.synchronize()
+    return (q, k, v, go), (dq, dk, dv)
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_matches_oracle(case):
+    name = case[0]
+    causal, window, scale = case[8], case[9], case[10]
+    print(f"[case] bwd {case}", flush=True)
+    (q, k, v, go), (dq, dk, dv) = run_case(case)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, go, causal=causal, window=window, scale=scale)
+    bq, bk, bv = error_bounds(q, k, v, go, causal, window, scale)
+    check(name + ".dq", dq, rq, bq)
+    check(name + ".dk", dk, rk, bk)
+    check(name + ".dv", dv, rv, bv)
+
+
+def test_bwd_no_keys_gives_zero_dq():
+    print("[case] bwd no keys", flush=True)
+    q, k, v = synth.gen_padded(230, 1, 2, 2, 40, 0, 128, "bf16")
+    go = synth.gen_grad(231, q.shape)
+    qd = q.to(DEV)
+    o, lse = fa.fwd(qd, k.to(DEV), v.to(DEV))
+    dq, dk, dv = fa.bwd(qd, k.to(DEV), v.to(DEV), o, go.to(DEV), lse)
+    torch.cuda.synchronize()
+    assert dq.float().abs().max().item() == 0.0 and dk.numel() == 0 and dv.numel() == 0
+
+
+def test_bwd_no_queries_gives_zero_dkdv():
+    print("[case] bwd no queries", flush=True)
+    q, k, v = synth.gen_padded(232, 1, 4, 2, 0, 100, 128, "bf16")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.empty_like(qd)
+    lse = torch.empty((1, 4, 0), dtype=torch.float32, device=DEV)
+    dk = torch.full_like(kd, 7.0)
+    dv = torch.full_like(vd, 7.0)
+    dq, dk, dv = fa.bwd(qd, kd, vd, o, torch.empty_like(qd), lse, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert dk.float().abs().max().item() == 0.0 and dv.float().abs().max().item() == 0.0
+
+
+def test_bwd_deterministic_bitwise():
+    """No atomics: two calls on the same inputs give identical bits."""
+    case = BWD_CASES[0]
+    print(f"[case] bwd determinism {case[0]}", flush=True)
+    _, g1 = run_case(case)
+    _, g2 = run_case(case)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
