@@ -5,7 +5,9 @@ A step is one call of the hot path on the headline workload: causal GQA
 prefill, B=4, Hq=32, Hkv=8, S=4096, d=128, bf16 (one fa_fwd launch).  The
 KV-cache decode workload (B=64, Hq=32, Hkv=8, d=128, cache lengths
 U{1024..32768}, split 1024 + combine) is timed beside it and reported under
-"decode".  Inputs are seeded synthetic tensors already resident in HBM.
+"decode", and the backward (fa_bwd, three kernels) of the prefill workload
+under "backward".  Inputs are seeded synthetic tensors already resident in
+HBM.
 
 Prints ONE JSON line (rank 0).  --gpus N with N > 1 is refused: this build
 runs on one GPU.
@@ -128,6 +130,35 @@ def bench_decode(steps, warmup):
     return res
 
 
+def bench_backward(steps, warmup, w):
+    """fa_bwd (three kernels) on the same workload, with the GPU forward's own
+    O and LSE and a seeded incoming gradient, all resident in HBM."""
+    q, k, v = synth.generate(w)
+    dev = "cuda:0"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    god = synth.gen_grad(w.seed + 1000, qd.shape, w.dtype).to(dev)
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, window=w.window)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    ws = torch.empty(max(fa.bwd_workspace_bytes(w.B, w.Hq, w.Sq), 16), dtype=torch.uint8, device=dev)
+    work = metrics.bwd_work(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window)
+
+    def step():
+        fa.bwd(qd, kd, vd, o, god, lse, causal=w.causal, window=w.window, dq=dq, dk=dk, dv=dv,
+               workspace=ws)
+
+    wall, ev = _timed(step, steps, warmup)
+    tf = work["flop"] / (ev * 1e-3) / 1e12
+    res = {"workload": w.name, "value": round(tf, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(wall, 4), "event_ms_per_call": round(ev, 4),
+           "frac_bf16_mfma_peak": round(tf / metrics.PEAK_BF16_TFLOPS, 4),
+           "algorithmic_flop": work["flop"], "kernels_per_call": 3,
+           "flop_convention": "10*d per visible pair per query head (2.5x forward)"}
+    del qd, kd, vd, god, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(q, k, v, w, budget_s: float):
     """The fp64 oracle on the host cores over whole (sequence, head) slices
     of the same workload, as many as fit in about budget_s seconds."""
@@ -162,6 +193,7 @@ def main():
     ap.add_argument("--workload", default="causal_gqa_prefill",
                     choices=[n for n, w in synth.WORKLOADS.items() if w.kind == "fwd"])
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -210,6 +242,8 @@ def main():
         del q
         line["decode"] = bench_decode(max(10, args.steps // 2), max(3, args.warmup // 2))
         q = None
+    if not args.no_backward:
+        line["backward"] = bench_backward(max(5, args.steps // 5), max(2, args.warmup // 5), w)
     if args.cpu_budget > 0:
         if q is None:
             q, k, v = synth.generate(w)

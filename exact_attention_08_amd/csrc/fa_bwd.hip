@@ -32,8 +32,9 @@
 //     A operand of reduction step b is one contiguous 1 KB read;
 //   * T order: the 8-byte slots ds_read_b64_tr_b16 reads, so the transposed
 //     operand (d x 16 rows) of a 32x32x16 MFMA is two contiguous 512 B reads.
-// A ring of 3 stages holds the tiles; one barrier per step publishes a stage
-// and frees the oldest one for the next copy.  The operands that stay fixed
+// A ring of stages holds the tiles (4 in the dK/dV kernel, whose stage also
+// carries the rows' LSE and D, 5 in the dQ kernel); one barrier per step
+// publishes a stage and frees the oldest one for the next copy.  The operands that stay fixed
 // for a work-group (K and V of the wave's keys in the dK/dV kernel, Q and dO
 // of the wave's rows in the dQ kernel) are loaded once into the accumulation
 // registers, which MFMAs read directly.
@@ -50,8 +51,23 @@ struct BwdGeo {
     static constexpr int DB = D / 32;            // 32-column blocks of d
     static constexpr int TE = R * D;             // elements per tile
     static constexpr int TB = TE * 2 / 1024;     // 1 KB blocks per tile
-    static constexpr int STAGES = 3;
 };
+constexpr int kDkdvStages = 4;   // ring depth of the dK/dV kernel (stage: 4 tiles + row terms)
+constexpr int kDqStages = 5;     // ring depth of the dQ kernel (stage: 3 tiles)
+
+// 4 bytes per lane from a buffer straight into LDS (buffer_load_dword ...
+// lds): lane i writes lds_base + 4*i; out-of-range offsets write zeros.  Not
+// tracked by the compiler (no destination registers): the caller waits
+// with s_waitcnt vmcnt before reading the LDS it fills.
+__device__ __forceinline__ void dma4_to_lds(i32x4 rsrc, uint32_t lds_base, int voffset) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %0, %1, 0 offen lds"
+        :
+        : "v"(voffset), "s"(rsrc), "s"(lds_base)
+        : "memory", "m0");
+}
 
 typedef __attribute__((address_space(3))) short bwd_lds_short;
 typedef short bwd_i16x4 __attribute__((ext_vector_type(4)));
@@ -157,8 +173,11 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 void fa_bwd_dkdv_kernel(BwdParams p) {
     using T = BwdGeo<D>;
     constexpr int TE = T::TE;
-    // stage s: Q (A order), dO (A order), Q (T order), dO (T order)
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[T::STAGES * 4 * TE];
+    // stage s: Q (A order), dO (A order), Q (T order), dO (T order), then
+    // the LSE and D of the block's rows (256 bytes each, the first 128 used)
+    constexpr int SE = 4 * TE + 256;             // stage size in 16-bit elements
+    constexpr int NS = kDkdvStages;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * SE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -210,10 +229,15 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     }
 
     // ---- copies of step s: Q and dO rows of query block qb_a + s % nqb of
-    // head hkv*G + s / nqb, in A and T order; tiles past the last step read
-    // nothing (zero records) so every step issues the same number of loads
+    // head hkv*G + s / nqb, in A and T order, and the LSE and D of those
+    // rows (every wave copies those two 256-byte pieces to the same place,
+    // so all waves issue the same number of loads); stages past the last
+    // step read nothing (zero records) so every step issues the same number
+    // of loads.  The row terms come through the copy path too: a plain
+    // vector load would complete in order behind the copies, and waiting
+    // for it would wait for every copy issued before it.
     constexpr int NB = 4 * T::TB;                // blocks per stage
-    constexpr int LPS = NB / T::NW;              // copies per wave per stage
+    constexpr int LPS = NB / T::NW + 2;          // copies per wave per stage
     static_assert(NB % T::NW == 0, "blocks split evenly over the waves");
     auto issue = [&](int s) __attribute__((always_inline)) {
         const bool valid = s < nsteps;
@@ -223,20 +247,24 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const long long off = (((long long)b * sq + i0) * p.Hq + h) * D * 2;
         const i32x4 qrs = uniform_rsrc(make_rsrc((const char*)p.q + off, rows * tok_q));
         const i32x4 ors = uniform_rsrc(make_rsrc((const char*)p.dout + off, rows * tok_q));
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + (s % T::STAGES) * 4 * TE));
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + (s % NS) * SE));
+        const long long rb = ((long long)b * p.Hq + h) * sq + i0;
+        dma4_to_lds(uniform_rsrc(make_rsrc(p.lse + rb, rows * 4)), dst + 4 * TE * 2, lane * 4);
+        dma4_to_lds(uniform_rsrc(make_rsrc(p.dsum + rb, rows * 4)), dst + 4 * TE * 2 + 256, lane * 4);
 #pragma unroll
-        for (int c = 0; c < LPS; ++c) {
+        for (int c = 0; c < LPS - 2; ++c) {
             const int blk = wave + c * T::NW;    // 0 .. NB-1
             const int tile = blk / T::TB, bb = blk % T::TB;   // tile 0 Q_A, 1 dO_A, 2 Q_T, 3 dO_T
             const int voff = tile < 2 ? a_order_off(bb, lane, tok_q) : t_order_off<T::DB>(bb, lane, tok_q);
             dma16_to_lds((tile & 1) ? ors : qrs, dst + tile * TE * 2 + bb * 1024, voff, 0);
         }
     };
-    // wait for this wave's copies of step s (those of step s+1 may still fly),
-    // then a barrier: every wave's copies of step s are visible and every
-    // wave is done with step s-1, whose stage step s+2 refills
+    // wait for this wave's copies of step s (those of steps s+1 .. s+NS-2
+    // may still fly), then a barrier: every wave's copies of step s are
+    // visible and every wave is done with step s-1, whose stage step s+NS-1
+    // refills
     auto sync_step = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS * (NS - 2)) : "memory");
     };
 
     f32x16 dkt[T::DB], dvt[T::DB];               // dK^T, dV^T: lane = key, element = d
@@ -246,37 +274,30 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) { dkt[db][e] = 0.f; dvt[db][e] = 0.f; }
 
     if (nsteps > 0) {
-        issue(0);
-        issue(1);
+        for (int s = 0; s < NS - 1; ++s) issue(s);
         for (int s = 0; s < nsteps; ++s) {
             sync_step();
-            issue(s + 2);
-            const int h = hkv * p.G + s / nqb;
+            issue(s + NS - 1);
             const int i0 = (qb_a + s % nqb) * T::R;
             // rows of this block that see a key of this wave: t = j - delta -
             // i spans [kw0 - delta - i0 - 31, kw0 + 31 - delta - i0]
             const int tmax = kw0 + T::R - 1 - delta - i0, tmin = kw0 - delta - i0 - (T::R - 1);
             if (tmax < t_lo || tmin > t_hi || kw0 >= sk) continue;   // uniform per wave
-            const uint16_t* st = ring + (s % T::STAGES) * 4 * TE;
+            const uint16_t* st = ring + (s % NS) * SE;
             const uint16_t* qa = st;
             const uint16_t* oa = st + TE;
             const uint16_t* qt = st + 2 * TE;
             const uint16_t* ot = st + 3 * TE;
+            const float* lse_s = reinterpret_cast<const float*>(st + 4 * TE);
+            const float* d_s = lse_s + 64;
 
             // LSE (log2 units) and D of rows i0 + acc_row(e) + 4g
             float lse2[16], dd[16];
             {
-                const long long rb = ((long long)b * p.Hq + h) * sq;
-                const int rows = max(min(sq - i0, T::R), 0);
-                const auto lrs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lse + rb + i0), (short)0,
-                                                                   rows * 4, 0x00020000);
-                const auto drs = __builtin_amdgcn_make_buffer_rsrc((void*)(p.dsum + rb + i0), (short)0,
-                                                                   rows * 4, 0x00020000);
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
-                    const int off = (8 * q4 + 4 * g) * 4;
-                    const f32x4 l4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(lrs, off, 0, 0));
-                    const f32x4 d4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0));
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * q4 + 4 * g);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 8 * q4 + 4 * g);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         // a row with no visible key has LSE = -inf: its
@@ -355,7 +376,8 @@ void fa_bwd_dq_kernel(BwdParams p) {
     using T = BwdGeo<D>;
     constexpr int TE = T::TE;
     // stage s: K (A order), V (A order), K (T order)
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[T::STAGES * 3 * TE];
+    constexpr int NS = kDqStages;
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * 3 * TE];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -436,7 +458,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         const long long off = kvbase + (long long)(valid ? jt : 0) * T::R * tok_kv;
         const i32x4 krs = uniform_rsrc(make_rsrc((const char*)p.k + off, rows * tok_kv));
         const i32x4 vrs = uniform_rsrc(make_rsrc((const char*)p.v + off, rows * tok_kv));
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + (s % T::STAGES) * 3 * TE));
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + (s % NS) * 3 * TE));
 #pragma unroll
         for (int c = 0; c < LPS; ++c) {
             const int blk = wave + c * T::NW;
@@ -446,7 +468,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         }
     };
     auto sync_step = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS * (NS - 2)) : "memory");
     };
 
     f32x16 dqt[T::DB];                                    // dQ^T: lane = row, element = d
@@ -456,13 +478,12 @@ void fa_bwd_dq_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) dqt[db][e] = 0.f;
 
     if (ntiles > 0) {
-        issue(0);
-        issue(1);
+        for (int s = 0; s < NS - 1; ++s) issue(s);
         for (int s = 0; s < ntiles; ++s) {
             sync_step();
-            issue(s + 2);
+            issue(s + NS - 1);
             const int jt = tile_lo + s;
-            const uint16_t* st = ring + (s % T::STAGES) * 3 * TE;
+            const uint16_t* st = ring + (s % NS) * 3 * TE;
             const uint16_t* ka = st;
             const uint16_t* va = st + TE;
             const uint16_t* kt = st + 2 * TE;

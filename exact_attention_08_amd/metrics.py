@@ -39,6 +39,17 @@ def fwd_work(B, Hq, Hkv, Sq, Sk, d, causal, window=(-1, -1), elem_bytes=2):
     return {"pairs": pairs, "flop": flop, "bytes": byts}
 
 
+def bwd_work(B, Hq, Hkv, Sq, Sk, d, causal, window=(-1, -1), elem_bytes=2):
+    """Gradients: five products of 2*d FLOP per visible (query, key) pair per
+    query head (S = Q K^T recomputed, dP = dO V^T, dV += P^T dO,
+    dK += dS^T Q, dQ += dS K), i.e. 2.5x the forward; bytes = Q, K, V, O, dO
+    and LSE read once and dQ, dK, dV written once."""
+    pairs = visible_pairs(Sq, Sk, causal, window)
+    flop = 10 * d * pairs * B * Hq
+    byts = (4 * B * Sq * Hq * d + 4 * B * Sk * Hkv * d) * elem_bytes + B * Hq * Sq * 4
+    return {"flop": flop, "bytes": byts, "pairs": pairs * B * Hq}
+
+
 def varlen_work(lengths_q, lengths_k, Hq, Hkv, d, causal, window=(-1, -1), elem_bytes=2):
     pairs = sum(Hq * visible_pairs(int(a), int(b), causal, window)
                 for a, b in zip(lengths_q, lengths_k))
