@@ -233,6 +233,96 @@ int fa_oracle_decode(const double* q, const double* kc, const double* vc,
     return err;
 }
 
+/* One-token decode against a paged KV cache, optionally appending the new
+ * token's key and value first.
+ *
+ * The pages say only that the fast library's cached-decode call supports a
+ * paged cache (project summary, feature list) and that paged layouts cut
+ * wasted cache memory (explainer, advice on generation with a cache).  The
+ * readings used here:
+ *   - the cache is a pool of num_pages pages of page_size token rows,
+ *     k_pages/v_pages: [num_pages, page_size, Hkv, d];
+ *   - block_table: [B, max_pages] page indices; token t of sequence b is row
+ *     t % page_size of page block_table[b][t / page_size];
+ *   - cache_seqlens[b] tokens are in the cache.  Without a new token the
+ *     query attends over those keys (as in fa_oracle_decode).  With k_new,
+ *     v_new ([B, Hkv, d], one new token per sequence) the new token is first
+ *     written at position cache_seqlens[b] (through the block table, into
+ *     k_pages/v_pages, which are therefore in/out), then the query attends
+ *     over cache_seqlens[b] + 1 keys.
+ * Keys are gathered one by one into a plain contiguous buffer and then
+ * attended exactly as in the contiguous decode above.
+ * Returns 0, -1 (allocation), -2 (head counts) or -3 (a position outside the
+ * table or a table entry outside the pool). */
+int fa_oracle_decode_paged(const double* q, double* k_pages, double* v_pages,
+                           const int32_t* block_table, const int32_t* cache_seqlens,
+                           const double* k_new, const double* v_new,
+                           double* out, double* lse,
+                           int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages,
+                           int d, int causal, int wl, int wr, double scale)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return -2;
+    int G = Hq / Hkv;
+    int append = k_new != NULL;
+    long cap = (long)max_pages * page_size;
+    for (int b = 0; b < B; ++b) {
+        long n = (long)cache_seqlens[b] + append;
+        if (cache_seqlens[b] < 0 || n > cap) return -3;
+        for (long t = 0; t < n; t += page_size) {
+            int pg = block_table[(long)b * max_pages + t / page_size];
+            if (pg < 0 || pg >= num_pages) return -3;
+        }
+    }
+    /* 1. append: the new row goes to position cache_seqlens[b] */
+    if (append) {
+        for (int b = 0; b < B; ++b) {
+            long t = cache_seqlens[b];
+            long pg = block_table[(long)b * max_pages + t / page_size];
+            long row = pg * page_size + t % page_size;
+            for (int g = 0; g < Hkv; ++g)
+                for (int c = 0; c < d; ++c) {
+                    k_pages[(row * Hkv + g) * d + c] = k_new[((long)b * Hkv + g) * d + c];
+                    v_pages[(row * Hkv + g) * d + c] = v_new[((long)b * Hkv + g) * d + c];
+                }
+        }
+    }
+    /* 2. attend over the sequence's keys, gathered page by page */
+    int err = 0;
+#pragma omp parallel
+    {
+        size_t rows = (size_t)(cap > 0 ? cap : 1);
+        double* scores = (double*)malloc(sizeof(double) * rows);
+        double* kseq = (double*)malloc(sizeof(double) * rows * (size_t)d);
+        double* vseq = (double*)malloc(sizeof(double) * rows * (size_t)d);
+        if (!scores || !kseq || !vseq) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic, 1)
+            for (int b = 0; b < B; ++b)
+                for (int h = 0; h < Hq; ++h) {
+                    long sk = (long)cache_seqlens[b] + append;
+                    int g = h / G;
+                    for (long t = 0; t < sk; ++t) {
+                        long pg = block_table[(long)b * max_pages + t / page_size];
+                        long row = pg * page_size + t % page_size;
+                        for (int c = 0; c < d; ++c) {
+                            kseq[t * d + c] = k_pages[(row * Hkv + g) * d + c];
+                            vseq[t * d + c] = v_pages[(row * Hkv + g) * d + c];
+                        }
+                    }
+                    attend_row(q + ((long)b * Hq + h) * d, kseq, vseq, d, 0, 1, sk, d,
+                               causal, wl, wr, scale, out + ((long)b * Hq + h) * d,
+                               lse + (long)b * Hq + h, scores);
+                }
+        }
+        free(scores);
+        free(kseq);
+        free(vseq);
+    }
+    return err;
+}
+
 /* Gradients of the padded-batch attention (the training backward).
  *
  * The "FlashAttention" explainer page, "Step 5" and "Backward pass in a bit

@@ -32,9 +32,13 @@ _lib_cache: dict[str, ctypes.CDLL] = {}
 
 def build(src: str = SRC, out: str = LIB, extra_flags: tuple[str, ...] = ()) -> str:
     """Compile the oracle with gcc (-O2, no fast-math, OpenMP over rows)."""
+    # build beside the target, then rename: a process loading the library
+    # meanwhile sees either the old file or the new one, never a partial one
+    tmp = f"{out}.{os.getpid()}.tmp"
     cmd = ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
-           *extra_flags, "-o", out, src, "-lm"]
+           *extra_flags, "-o", tmp, src, "-lm"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, out)
     return out
 
 
@@ -51,8 +55,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                      i32, i32, i32, f64]
     lib.fa_oracle_bwd.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                   i32, i32, i32, f64]
+    lib.fa_oracle_decode_paged.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
+                                           i32, i32, i32, i32, i32, i32, f64]
     for f in (lib.fa_oracle_rows, lib.fa_oracle_fwd, lib.fa_oracle_varlen,
-              lib.fa_oracle_decode, lib.fa_oracle_bwd):
+              lib.fa_oracle_decode, lib.fa_oracle_bwd, lib.fa_oracle_decode_paged):
         f.restype = ctypes.c_int
     return lib
 
@@ -66,6 +72,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
             if path != LIB:
                 raise FileNotFoundError(path)
             build()
+        elif path == LIB and os.path.getmtime(path) < os.path.getmtime(SRC):
+            build()   # the source changed since the library was built
         lib = _bind(ctypes.CDLL(path))
         _lib_cache[path] = lib
         return lib
@@ -184,6 +192,37 @@ class Oracle:
             raise RuntimeError(f"oracle decode failed: {rc}")
         return out, lse
 
+    # -- decode against a paged cache, with an optional append ---------------
+    def attention_decode_paged(self, q, k_pages, v_pages, block_table, cache_seqlens,
+                               k_new=None, v_new=None, causal=False, window=(-1, -1),
+                               scale=None):
+        """q: [B,1,Hq,d]; pages: [num_pages,page_size,Hkv,d]; block_table:
+        [B,max_pages]; cache_seqlens: [B] tokens in the cache; k_new, v_new:
+        [B,1,Hkv,d] or None.  The caller's pages are not modified.
+        -> (out [B,1,Hq,d], lse [B,Hq], k_pages', v_pages') where the primed
+        pages hold the appended rows."""
+        q = _f64(q)
+        kp, vp = _f64(k_pages).copy(), _f64(v_pages).copy()
+        bt, sl = _i32(block_table), _i32(cache_seqlens)
+        B, one, Hq, d = q.shape
+        assert one == 1
+        num_pages, page_size, Hkv, _ = kp.shape
+        assert bt.ndim == 2 and bt.shape[0] == B and sl.shape == (B,)
+        kn = vn = None
+        if k_new is not None:
+            kn, vn = _f64(k_new), _f64(v_new)
+            assert kn.shape == (B, 1, Hkv, d) and vn.shape == kn.shape
+        out = np.empty_like(q)
+        lse = np.empty((B, Hq), dtype=np.float64)
+        rc = self.lib.fa_oracle_decode_paged(
+            _ptr(q), _ptr(kp), _ptr(vp), _ptr(bt), _ptr(sl),
+            _ptr(kn) if kn is not None else None, _ptr(vn) if vn is not None else None,
+            _ptr(out), _ptr(lse), B, Hq, Hkv, num_pages, page_size, bt.shape[1], d,
+            int(bool(causal)), int(window[0]), int(window[1]), _scale(scale, d))
+        if rc != 0:
+            raise RuntimeError(f"oracle paged decode failed: {rc}")
+        return out, lse, kp, vp
+
     # -- sampled rows of one (sequence, head) ------------------------------
     def attention_rows(self, q_rows, qi, sq, k_seq, v_seq, causal=False,
                        window=(-1, -1), scale=None):
@@ -225,6 +264,10 @@ def attention_varlen(*a, **kw):
 
 def attention_decode(*a, **kw):
     return default().attention_decode(*a, **kw)
+
+
+def attention_decode_paged(*a, **kw):
+    return default().attention_decode_paged(*a, **kw)
 
 
 def attention_bwd(*a, **kw):

@@ -546,6 +546,102 @@ def pin_bwd_gqa_equals_repeated_mha(orc):
     assert np.abs(dv - dv2.reshape(B, Sk, Hkv, G, d).sum(3)).max() < 1e-12
 
 
+def _paginate(rng, cache, lens, page_size, spare_pages=2):
+    """Scatter a contiguous cache [B, cap, Hkv, d] into a shuffled page pool
+    (each sequence's first ceil(len/page_size) pages, in random physical
+    order, plus unreferenced spare pages of random data).  Pages are cut by
+    reshaping each sequence's rows; table entries past a sequence's pages
+    hold an index outside the pool, so reading one is an error.
+    -> (pages [num_pages, page_size, Hkv, d], block_table [B, max_pages])."""
+    B, cap, Hkv, d = cache.shape
+    assert cap % page_size == 0
+    need = [-(-int(n) // page_size) for n in lens]
+    max_pages = max(max(need), 1)
+    num_pages = sum(need) + spare_pages
+    perm = rng.permutation(num_pages)
+    pages = _rand(rng, num_pages, page_size, Hkv, d)
+    table = np.full((B, max_pages), num_pages + 7, dtype=np.int32)
+    nxt = 0
+    for b in range(B):
+        chunks = cache[b].reshape(cap // page_size, page_size, Hkv, d)
+        for pg in range(need[b]):
+            pages[perm[nxt]] = chunks[pg]
+            table[b, pg] = perm[nxt]
+            nxt += 1
+    return pages, table
+
+
+def pin_paged_equals_contiguous(orc):
+    """A paged cache (shuffled pages, garbage in unused rows and spare pages)
+    gives exactly the contiguous-cache decode of the same keys."""
+    rng = _rng(60)
+    B, Hq, Hkv, d = 3, 4, 2, 5
+    for page_size, lens in [(1, [3, 0, 5]), (3, [9, 4, 1]), (4, [8, 7, 12]), (8, [16, 1, 9])]:
+        cap = page_size * -(-max(lens) // page_size)
+        lens = np.array(lens, dtype=np.int32)
+        q = _rand(rng, B, 1, Hq, d)
+        kc = _rand(rng, B, cap, Hkv, d); vc = _rand(rng, B, cap, Hkv, d)
+        pk, table = _paginate(np.random.default_rng(page_size), kc, lens, page_size)
+        pv, table_v = _paginate(np.random.default_rng(page_size), vc, lens, page_size)
+        assert np.array_equal(table, table_v)
+        for (wl, wr) in [(-1, -1), (2, -1)]:
+            o1, l1, pk2, pv2 = orc.attention_decode_paged(q, pk, pv, table, lens, causal=True,
+                                                          window=(wl, wr), scale=0.6)
+            o2, l2 = orc.attention_decode(q, kc, vc, lens, causal=True, window=(wl, wr), scale=0.6)
+            assert np.array_equal(o1, o2) and np.array_equal(l1, l2), (page_size, wl)
+            assert np.array_equal(pk2, pk) and np.array_equal(pv2, pv)   # nothing appended
+
+
+def pin_paged_append(orc):
+    """Appending writes the new key/value row at position cache_seqlens[b]
+    of its sequence (and nowhere else), and the query then sees that row:
+    the result equals the contiguous decode over the cache with the row in
+    place and one more key."""
+    rng = _rng(61)
+    B, Hq, Hkv, d, page_size = 3, 6, 2, 4, 4
+    lens = np.array([0, 7, 8], dtype=np.int32)            # empty, mid-page, page boundary
+    cap = 12
+    q = _rand(rng, B, 1, Hq, d)
+    kc = _rand(rng, B, cap, Hkv, d); vc = _rand(rng, B, cap, Hkv, d)
+    kn = _rand(rng, B, 1, Hkv, d); vn = _rand(rng, B, 1, Hkv, d)
+    kc2, vc2 = kc.copy(), vc.copy()
+    for b in range(B):
+        kc2[b, lens[b]] = kn[b, 0]
+        vc2[b, lens[b]] = vn[b, 0]
+    # pages hold the old contents (row lens[b] is stale) for len+1 rows
+    pk, table = _paginate(np.random.default_rng(5), kc, lens + 1, page_size)
+    pv, _ = _paginate(np.random.default_rng(5), vc, lens + 1, page_size)
+    pk_want, _ = _paginate(np.random.default_rng(5), kc2, lens + 1, page_size)
+    pv_want, _ = _paginate(np.random.default_rng(5), vc2, lens + 1, page_size)
+    for (wl, wr) in [(-1, -1), (3, -1)]:
+        o1, l1, pk2, pv2 = orc.attention_decode_paged(q, pk, pv, table, lens, kn, vn, causal=True,
+                                                      window=(wl, wr), scale=0.45)
+        o2, l2 = orc.attention_decode(q, kc2, vc2, lens + 1, causal=True, window=(wl, wr),
+                                      scale=0.45)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), wl
+        assert np.array_equal(pk2, pk_want) and np.array_equal(pv2, pv_want)
+
+
+def pin_paged_append_zero_query(orc):
+    """Q = 0 with an append: LSE = ln(cache_seqlens + 1) and O is the mean
+    of the cached V rows and the new one."""
+    rng = _rng(62)
+    B, Hq, Hkv, d, page_size = 2, 2, 1, 3, 2
+    lens = np.array([4, 1], dtype=np.int32)
+    kc = _rand(rng, B, 6, Hkv, d); vc = _rand(rng, B, 6, Hkv, d)
+    kn = _rand(rng, B, 1, Hkv, d); vn = _rand(rng, B, 1, Hkv, d)
+    pk, table = _paginate(np.random.default_rng(9), kc, lens + 1, page_size)
+    pv, _ = _paginate(np.random.default_rng(9), vc, lens + 1, page_size)
+    out, lse, _, _ = orc.attention_decode_paged(np.zeros((B, 1, Hq, d)), pk, pv, table, lens,
+                                                kn, vn)
+    for b in range(B):
+        L = int(lens[b])
+        mean = (vc[b, :L, 0].sum(0) + vn[b, 0, 0]) / (L + 1)
+        for h in range(Hq):
+            assert abs(lse[b, h] - math.log(L + 1)) < 1e-13
+            assert np.abs(out[b, 0, h] - mean).max() < 1e-13
+
+
 PINS = [
     pin_worked_example, pin_torch_sdpa, pin_zero_query_closed_form, pin_varlen_zero_query,
     pin_decode_zero_query, pin_constant_v, pin_single_visible_key, pin_one_hot_values,
@@ -553,5 +649,6 @@ PINS = [
     pin_varlen_equals_per_sequence, pin_decode_equals_last_prefill_row, pin_key_translation,
     pin_split_combine, pin_fully_masked_rows, pin_large_scores_stable, pin_mpmath_brute_force,
     pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_identities,
-    pin_bwd_gqa_equals_repeated_mha,
+    pin_bwd_gqa_equals_repeated_mha, pin_paged_equals_contiguous, pin_paged_append,
+    pin_paged_append_zero_query,
 ]

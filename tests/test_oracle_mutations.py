@@ -52,6 +52,19 @@ MUTANTS = {
     "bwd_first_group_head_only": ("for (int h = g * G; h < (g + 1) * G; ++h)",
                                   "for (int h = g * G; h < g * G + 1; ++h)"),
     "bwd_dv_from_queries": ("dvrow[c] += p[j] * gorow[c];", "dvrow[c] += p[j] * qrow[c];"),
+    "paged_gather_ignores_table": (
+        "                        long pg = block_table[(long)b * max_pages + t / page_size];",
+        "                        long pg = (long)b * max_pages + t / page_size;"),
+    "paged_table_row_stride": (
+        "                        long pg = block_table[(long)b * max_pages + t / page_size];",
+        "                        long pg = block_table[(long)b + t / page_size];"),
+    "paged_row_ignores_offset": ("                        long row = pg * page_size + t % page_size;",
+                                 "                        long row = pg * page_size;"),
+    "append_not_seen": ("long sk = (long)cache_seqlens[b] + append;", "long sk = (long)cache_seqlens[b];"),
+    "append_value_from_key": ("v_pages[(row * Hkv + g) * d + c] = v_new[((long)b * Hkv + g) * d + c];",
+                              "v_pages[(row * Hkv + g) * d + c] = k_new[((long)b * Hkv + g) * d + c];"),
+    "append_head_ignored": ("k_pages[(row * Hkv + g) * d + c] = k_new[((long)b * Hkv + g) * d + c];",
+                            "k_pages[(row * Hkv + g) * d + c] = k_new[((long)b * Hkv) * d + c];"),
 }
 
 

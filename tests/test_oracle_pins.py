@@ -7,8 +7,7 @@ from oracle_pins import PINS
 
 @pytest.fixture(scope="module")
 def orc():
-    oracle.build()
-    return oracle.Oracle(oracle.load())
+    return oracle.Oracle(oracle.load())   # builds when missing or older than its source
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
