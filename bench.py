@@ -5,8 +5,10 @@ A step is one call of the hot path on the headline workload: causal GQA
 prefill, B=4, Hq=32, Hkv=8, S=4096, d=128, bf16 (one fa_fwd launch).  The
 KV-cache decode workload (B=64, Hq=32, Hkv=8, d=128, cache lengths
 U{1024..32768}, split 1024 + combine) is timed beside it and reported under
-"decode", and the backward (fa_bwd, three kernels) of the prefill workload
-under "backward".  Inputs are seeded synthetic tensors already resident in
+"decode"; the same keys in a shuffled pool of 256-row pages, with each
+sequence's last key appended by the call (fa_decode_paged: append, split,
+combine), under "decode_paged"; and the backward (fa_bwd, three kernels) of
+the prefill workload under "backward".  Inputs are seeded synthetic tensors already resident in
 HBM.
 
 Prints ONE JSON line (rank 0).  --gpus N with N > 1 is refused: this build
@@ -130,6 +132,43 @@ def bench_decode(steps, warmup):
     return res
 
 
+def bench_decode_paged(steps, warmup, page_size=256):
+    """fa_decode_paged on the decode workload's keys and values: the same
+    drawn lengths and rows cut into pages of page_size rows placed in a
+    shuffled pool; each sequence's last key arrives as the appended new
+    token (written into its page by the call, then attended), so the
+    attended keys, and the algorithmic bytes, are those of the contiguous
+    decode."""
+    w = synth.WORKLOADS["kvcache_decode"]
+    q, kp, vp, bt, sl, kn, vn, lens = synth.gen_paged(
+        w.seed, w.B, w.Hq, w.Hkv, w.d, page_size, w.len_range[0], w.len_range[1], w.dtype,
+        w.sigma, append=True)
+    dev = "cuda:0"
+    qd, kpd, vpd, btd, sld, knd, vnd = (x.to(dev) for x in (q, kp, vp, bt, sl, kn, vn))
+    del kp, vp
+    mx = int(lens.max())
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.Hq, mx, w.d, w.split), dtype=torch.uint8,
+                     device=dev)
+    work = metrics.decode_work(lens.tolist(), w.Hq, w.Hkv, w.d)
+
+    def step():
+        fa.decode_paged(qd, kpd, vpd, btd, sld, mx, k_new=knd, v_new=vnd, split_size=w.split,
+                        out=out, lse=lse, workspace=ws)
+
+    wall, ev = _timed(step, steps, warmup)
+    gbs = work["bytes"] / (ev * 1e-3) / 1e9
+    res = {"workload": w.name + f"_paged{page_size}_append", "value": round(gbs, 1), "unit": "GB/s",
+           "ms_per_step": round(wall, 4), "event_ms_per_call": round(ev, 4),
+           "frac_hbm_peak": round(gbs / metrics.PEAK_HBM_GBS, 4),
+           "algorithmic_bytes": work["bytes"], "kernels_per_call": 3,
+           "page_size": page_size, "num_pages": int(kpd.shape[0])}
+    del qd, kpd, vpd, btd, sld, knd, vnd
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_backward(steps, warmup, w):
     """fa_bwd (three kernels) on the same workload, with the GPU forward's own
     O and LSE and a seeded incoming gradient, all resident in HBM."""
@@ -241,6 +280,7 @@ def main():
     if not args.no_decode:
         del q
         line["decode"] = bench_decode(max(10, args.steps // 2), max(3, args.warmup // 2))
+        line["decode_paged"] = bench_decode_paged(max(10, args.steps // 2), max(3, args.warmup // 2))
         q = None
     if not args.no_backward:
         line["backward"] = bench_backward(max(5, args.steps // 5), max(2, args.warmup // 5), w)

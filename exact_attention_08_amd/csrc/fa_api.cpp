@@ -202,6 +202,66 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
     return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
 }
 
+fa_status_t fa_decode_paged(const void* q, void* k_pages, void* v_pages,
+                            const int32_t* block_table, const int32_t* cache_seqlens,
+                            const void* k_new, const void* v_new, void* out, float* lse,
+                            int B, int Hq, int Hkv, int num_pages, int page_size,
+                            int max_pages_per_seq, int max_seqlen_k, int d, int causal,
+                            int window_left, int window_right, float softmax_scale,
+                            int split_size, void* workspace, size_t workspace_bytes,
+                            fa_dtype_t dtype, hipStream_t stream) {
+    fa_status_t st = check_common(q, k_pages, v_pages, out, lse, B, Hq, Hkv, d, window_left,
+                                  window_right, softmax_scale, dtype);
+    if (st != FA_OK) return st;
+    if (!block_table || !aligned4(block_table))
+        return fail(FA_ERR_INVALID_ARG, "block_table must be non-null and 4-byte aligned");
+    if (!cache_seqlens || !aligned4(cache_seqlens))
+        return fail(FA_ERR_INVALID_ARG, "cache_seqlens must be non-null and 4-byte aligned");
+    if ((k_new == nullptr) != (v_new == nullptr))
+        return fail(FA_ERR_INVALID_ARG, "k_new and v_new must both be given or both be NULL");
+    if (k_new && (!aligned16(k_new) || !aligned16(v_new)))
+        return fail(FA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+    if (page_size < 32 || page_size % 32 != 0)
+        return fail(FA_ERR_INVALID_ARG, "page_size must be a positive multiple of 32 (got %d)",
+                    page_size);
+    if (num_pages < 1 || max_pages_per_seq < 1)
+        return fail(FA_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be >= 1 (got %d, %d)",
+                    num_pages, max_pages_per_seq);
+    const long long cap = (long long)max_pages_per_seq * page_size;
+    if (max_seqlen_k < 1 || max_seqlen_k > cap)
+        return fail(FA_ERR_INVALID_ARG,
+                    "max_seqlen_k must be in [1, max_pages_per_seq * page_size] (got %d)",
+                    max_seqlen_k);
+    if (split_size < 64 || split_size % 64 != 0)
+        return fail(FA_ERR_INVALID_ARG, "split_size must be a positive multiple of 64 (got %d)",
+                    split_size);
+    const size_t need = fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d, split_size);
+    if (!workspace || !aligned16(workspace))
+        return fail(FA_ERR_WORKSPACE, "workspace must be non-null and 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    fa::DecodeParams p{};
+    p.q = q; p.k = k_pages; p.v = v_pages; p.o = out; p.lse = lse;
+    p.seqlens = cache_seqlens;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sk_cap = 0;                               // unused with a block table
+    p.max_len = max_seqlen_k;
+    p.split = split_size;
+    p.nsplit = (max_seqlen_k + split_size - 1) / split_size;
+    p.qblocks = (p.G + 15) / 16;
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = p.ws_o + (size_t)B * Hq * p.nsplit * d;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    set_scale(softmax_scale, &p.c, &p.qsign);
+    p.block_table = block_table;
+    p.page_size = page_size; p.max_pages = max_pages_per_seq; p.num_pages = num_pages;
+    p.append = k_new != nullptr;
+    p.k_new = k_new; p.v_new = v_new;
+    if ((long long)p.nsplit * p.qblocks * Hkv * B * fa::kDecodeThreads > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq) {
     if (B < 1 || Hq < 1 || Sq < 1) return 0;
     return (size_t)B * Hq * Sq * sizeof(float);

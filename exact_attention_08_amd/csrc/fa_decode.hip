@@ -31,6 +31,16 @@
 // Combine kernel: one wave per (sequence, query head); with M = max_c LSE_c,
 // w_c = exp(LSE_c - M): LSE = M + ln(sum w_c), O = sum w_c O_c / sum w_c,
 // summed in split order (deterministic), several partial rows in flight.
+//
+// Paged cache (the project summary's "paged KV cache support"; the
+// explainer's advice to use paged cache layouts): the keys of sequence b
+// live in pages of page_size token rows, token t at row t % page_size of
+// page block_table[b][t / page_size].  page_size is a multiple of 32, so
+// each 32-key block of the split kernel lies in one page and costs one
+// table read; the buffer resource of a block then starts at that page row.
+// With an append, a small kernel first writes the new token's key and value
+// row at position cache_seqlens[b], and the split and combine kernels see
+// one more key.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -38,7 +48,38 @@ namespace fa {
 
 constexpr float kDecodeRescaleThreshold = 8.0f;   // log2 units, as in the forward kernel
 
-template <int D, bool BF16>
+// Keys sequence b attends over: its cache length clamped to [0, max_len], or
+// with an append the clamped position of the new token plus one.
+__device__ __forceinline__ int decode_len(const DecodeParams& p, int b) {
+    const int s = p.seqlens[b];
+    return p.append ? min(max(s, 0), p.max_len - 1) + 1 : min(max(s, 0), p.max_len);
+}
+
+// The new token's key and value rows into their page (one thread per
+// 16-byte chunk of a (sequence, K/V head) row).  A table entry outside the
+// pool writes nothing.
+template <int D>
+__global__ __launch_bounds__(256) void fa_decode_append_kernel(DecodeParams p) {
+    constexpr int CH = D / 8;
+    const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (long long)p.B * p.Hkv * CH) return;
+    const int c = (int)(t % CH);
+    const long long bh = t / CH;
+    const int hkv = (int)(bh % p.Hkv), b = (int)(bh / p.Hkv);
+    const int pos = decode_len(p, b) - 1;
+    const int pg = pos / p.page_size;
+    const int phys = p.block_table[(long long)b * p.max_pages + pg];
+    if (phys < 0 || phys >= p.num_pages) return;
+    const long long row = (long long)phys * p.page_size + (pos - pg * p.page_size);
+    const long long dst = (row * p.Hkv + hkv) * D + c * 8;
+    const long long src = ((long long)b * p.Hkv + hkv) * D + c * 8;
+    *reinterpret_cast<u32x4*>((uint16_t*)const_cast<void*>(p.k) + dst) =
+        *reinterpret_cast<const u32x4*>((const uint16_t*)p.k_new + src);
+    *reinterpret_cast<u32x4*>((uint16_t*)const_cast<void*>(p.v) + dst) =
+        *reinterpret_cast<const u32x4*>((const uint16_t*)p.v_new + src);
+}
+
+template <int D, bool BF16, bool PAGED>
 __global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_decode_split_kernel(DecodeParams p) {
     constexpr int KS = D / 32;            // reduction steps over d (16x16x32)
@@ -66,7 +107,7 @@ void fa_decode_split_kernel(DecodeParams p) {
     const int qb = i % p.qblocks; i /= p.qblocks;
     const int split_idx = i % p.nsplit;
     const int b = i / p.nsplit;
-    const int L = min(max(p.seqlens[b], 0), p.max_len);
+    const int L = decode_len(p, b);
     if (split_idx >= (L + p.split - 1) / p.split) return;   // uniform over the work-group
 
     // The query sits at key position L-1: causal and the right window never
@@ -99,12 +140,34 @@ void fa_decode_split_kernel(DecodeParams p) {
 
     // Buffer resource over keys [jb, kb) of this sequence (all heads); rows
     // at or past kb read as zeros, so no load leaves the cache (a block past
-    // kb reads nothing at all).
-    auto block_rows = [&](int jb) __attribute__((always_inline)) {
-        return max(kb - jb, 0) * tok_bytes;
+    // kb reads nothing at all).  Paged: the 32 keys of block jb lie in one
+    // page; the resource starts at the block's row of that page and covers
+    // at most 32 rows; a block past kb reads no table entry, and a table
+    // entry outside the pool reads zeros.
+    struct Span { const char* ptr; int bytes; };
+    auto block_span = [&](const void* base, int jb) __attribute__((always_inline)) {
+        if constexpr (PAGED) {
+            int rows = min(kb - jb, 32);
+            long long off = 0;
+            if (rows > 0) {
+                const int pg = jb / p.page_size;
+                const int phys = p.block_table[(long long)b * p.max_pages + pg];
+                if (phys >= 0 && phys < p.num_pages)
+                    off = ((long long)phys * p.page_size + (jb - pg * p.page_size)) * tok_bytes;
+                else
+                    rows = 0;
+            } else {
+                rows = 0;
+            }
+            return Span{(const char*)base + off, rows * tok_bytes};
+        } else {
+            return Span{(const char*)base + seq_bytes + (long long)jb * tok_bytes,
+                        max(kb - jb, 0) * tok_bytes};
+        }
     };
     auto block_rsrc = [&](const void* base, int jb) __attribute__((always_inline)) {
-        return make_rsrc((const char*)base + seq_bytes + (long long)jb * tok_bytes, block_rows(jb));
+        const Span sp = block_span(base, jb);
+        return make_rsrc(sp.ptr, sp.bytes);
     };
     // K rows in LDS: 16-byte chunk c of row r sits at chunk slot c ^ swz(r),
     // so the 16 rows one MFMA operand read touches hit 16 distinct bank
@@ -135,9 +198,8 @@ void fa_decode_split_kernel(DecodeParams p) {
     // 16 lanes a whole row.  Keys before ka read as zeros (offset past the
     // resource), keys at or past kb through the resource bound.
     auto load_v = [&](VBlock& blk, int jb) __attribute__((always_inline)) {
-        const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const char*)p.v + seq_bytes + (long long)jb * tok_bytes), (short)0,
-            block_rows(jb), 0x00020000);
+        const Span sp = block_span(p.v, jb);
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc((void*)sp.ptr, (short)0, sp.bytes, 0x00020000);
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
             const int r = slot_key(sl);
@@ -330,13 +392,23 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
     const int lane = threadIdx.x & 63;
     if (w >= p.B * p.Hq) return;
     const int b = w / p.Hq, hq = w - b * p.Hq;
-    const int L = min(max(p.seqlens[b], 0), p.max_len);
+    const int L = decode_len(p, b);
     const int n = (L + p.split - 1) / p.split;
     const long long row0 = ((long long)b * p.Hq + hq) * p.nsplit;
+    const float* src = p.ws_o + row0 * D + lane * PER;
+
+    // The first 64 LSEs (lane s: split s) and the first UNROLL partial rows
+    // are requested together: the rows do not depend on the weights.
+    float lse0 = lane < n ? p.ws_lse[row0 + lane] : -INFINITY;
+    float x0[UNROLL][PER];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) x0[k][u] = k < n ? src[(long long)k * D + u] : 0.f;
 
     // M = max_c LSE_c, lanes over splits
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < n; s0 += 64)
+    float M = lse0;
+    for (int s0 = 64; s0 < n; s0 += 64)
         if (s0 + lane < n) M = fmaxf(M, p.ws_lse[row0 + s0 + lane]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -346,17 +418,24 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
     for (int u = 0; u < PER; ++u) acc[u] = 0.f;
     float sum = 0.f;
     if (M != -INFINITY) {
-        const float* src = p.ws_o + row0 * D + lane * PER;
+        // lane s holds the weight of split s0 + s; the sums below run in
+        // split order (deterministic)
+        auto weight = [&](float ls) { return ls == -INFINITY ? 0.f : exp2_fast((ls - M) * kLog2e); };
+        auto add_row = [&](float wl, int k, const float* x) __attribute__((always_inline)) {
+            const float wk = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
+            sum += wk;
+#pragma unroll
+            for (int u = 0; u < PER; ++u) acc[u] = fmaf(wk, x[u], acc[u]);
+        };
+        float wl = weight(lse0);
+#pragma unroll
+        for (int k = 0; k < UNROLL; ++k)
+            if (k < n) add_row(wl, k, x0[k]);
         for (int s0 = 0; s0 < n; s0 += 64) {
-            // lane s holds the weight of split s0 + s; the sums below run
-            // in split order (deterministic)
-            float wl = 0.f;
-            if (s0 + lane < n) {
-                const float ls = p.ws_lse[row0 + s0 + lane];
-                wl = ls == -INFINITY ? 0.f : exp2_fast((ls - M) * kLog2e);
-            }
+            if (s0 > 0) wl = s0 + lane < n ? weight(p.ws_lse[row0 + s0 + lane]) : 0.f;
             const int m = min(64, n - s0);
-            for (int c0 = 0; c0 < m; c0 += UNROLL) {
+            for (int c0 = s0 == 0 ? UNROLL : 0; c0 < m; c0 += UNROLL) {
                 float x[UNROLL][PER];
 #pragma unroll
                 for (int k = 0; k < UNROLL; ++k)
@@ -364,15 +443,8 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
                     for (int u = 0; u < PER; ++u)
                         x[k][u] = c0 + k < m ? src[(long long)(s0 + c0 + k) * D + u] : 0.f;
 #pragma unroll
-                for (int k = 0; k < UNROLL; ++k) {
-                    if (c0 + k < m) {
-                        const float wk = __builtin_bit_cast(
-                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), c0 + k));
-                        sum += wk;
-#pragma unroll
-                        for (int u = 0; u < PER; ++u) acc[u] = fmaf(wk, x[k][u], acc[u]);
-                    }
-                }
+                for (int k = 0; k < UNROLL; ++k)
+                    if (c0 + k < m) add_row(wl, c0 + k, x[k]);
             }
         }
     }
@@ -390,9 +462,18 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
 
 template <int D, bool BF16>
 static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
+    if (p.append) {
+        const long long n = (long long)p.B * p.Hkv * (D / 8);
+        hipLaunchKernelGGL((fa_decode_append_kernel<D>), dim3((unsigned)((n + 255) / 256)), dim3(256),
+                           0, s, p);
+    }
     const long long nsplit_blocks = (long long)p.nsplit * p.qblocks * p.Hkv * p.B;
-    hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16>), dim3((unsigned)nsplit_blocks),
-                       dim3(kDecodeThreads), 0, s, p);
+    if (p.block_table != nullptr)
+        hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16, true>), dim3((unsigned)nsplit_blocks),
+                           dim3(kDecodeThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((fa_decode_split_kernel<D, BF16, false>), dim3((unsigned)nsplit_blocks),
+                           dim3(kDecodeThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const long long ncomb = ((long long)p.B * p.Hq + 3) / 4;

@@ -49,6 +49,14 @@ struct DecodeParams {
     int causal, wl, wr;
     float c;                    // |scale| * log2(e)
     uint32_t qsign;
+    // paged cache (k, v point at the page pools [num_pages, page_size, Hkv, d])
+    const int32_t* block_table; // [B, max_pages]; null for a contiguous cache
+    int page_size, max_pages, num_pages;
+    // append: k_new, v_new [B, Hkv, d] are written at position seqlens[b]
+    // (clamped to max_len - 1) and seen as one more key
+    int append;
+    const void* k_new;
+    const void* v_new;
 };
 
 // Backward (gradients): row-term kernel, dK/dV kernel, dQ kernel.

@@ -24,7 +24,8 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_E
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
-           "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str", "fa_last_error")
+           "fa_decode_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+           "fa_last_error")
 
 _lock = threading.Lock()
 _lib = None
@@ -59,6 +60,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_decode_kvcache.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
                                           ctypes.c_size_t, I, P]
         lib.fa_decode_kvcache.restype = I
+        lib.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I,
+                                        F, I, P, ctypes.c_size_t, I, P]
+        lib.fa_decode_paged.restype = I
         lib.fa_bwd_workspace_bytes.argtypes = [I, I, I]
         lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P,
@@ -177,6 +181,48 @@ def decode_kvcache(q, k_cache, v_cache, cache_seqlens, max_seqlen_k, *, causal=F
                                  _scale(softmax_scale, d), int(split_size), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(),
                                  _DTYPE[q.dtype], _stream()))
+    return out, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, max_seqlen_k, *, k_new=None,
+                 v_new=None, causal=False, window=(-1, -1), softmax_scale=None, split_size=1024,
+                 out=None, lse=None, workspace=None):
+    """One-token decode against a paged cache: q [B,1,Hq,d], page pools
+    [num_pages,page_size,Hkv,d], block_table int32 [B,max_pages], cache_seqlens int32 [B]
+    (tokens in the cache), optional k_new/v_new [B,1,Hkv,d] appended in place at
+    position cache_seqlens[b] before attending -> (out [B,1,Hq,d], lse [B,Hq] fp32)."""
+    _check_tensors(q, k_pages, v_pages)
+    _require(q.dim() == 4 and q.shape[1] == 1, "q must be [B,1,Hq,d]")
+    _require(k_pages.dim() == 4 and k_pages.shape == v_pages.shape,
+             "page pools must be [num_pages,page_size,Hkv,d]")
+    _require(block_table.is_cuda and block_table.dtype == torch.int32 and block_table.dim() == 2
+             and block_table.is_contiguous(), "block_table must be a contiguous int32 [B,max_pages] GPU tensor")
+    _require(cache_seqlens.is_cuda and cache_seqlens.dtype == torch.int32,
+             "cache_seqlens must be an int32 GPU vector")
+    B, _, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_pages.shape
+    _require(block_table.shape[0] == B, "block_table must have B rows")
+    if k_new is not None or v_new is not None:
+        _require(k_new is not None and v_new is not None, "give both k_new and v_new")
+        _check_tensors(k_new, v_new)
+        _require(tuple(k_new.shape) == (B, 1, Hkv, d) and v_new.shape == k_new.shape,
+                 "k_new, v_new must be [B,1,Hkv,d]")
+    lib = load()
+    need = int(lib.fa_decode_workspace_bytes(B, Hq, int(max_seqlen_k), d, int(split_size)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                               _ptr(cache_seqlens), _ptr(k_new) if k_new is not None else None,
+                               _ptr(v_new) if v_new is not None else None, _ptr(out), _ptr(lse),
+                               B, Hq, Hkv, num_pages, page_size, block_table.shape[1],
+                               int(max_seqlen_k), d, int(bool(causal)), int(window[0]),
+                               int(window[1]), _scale(softmax_scale, d), int(split_size),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _DTYPE[q.dtype], _stream()))
     return out, lse
 
 

@@ -139,6 +139,56 @@ def gen_decode(seed: int, B: int, Hq: int, Hkv: int, d: int, Sk_cap: int, lo: in
     return q, kc, vc, lengths.to(torch.int32)
 
 
+def gen_paged(seed: int, B: int, Hq: int, Hkv: int, d: int, page_size: int, lo: int, hi: int,
+              dtype: str = "bf16", sigma: float = 1.0, lengths=None, append: bool = True,
+              spare_pages: int = 0):
+    """Paged-cache decode inputs.  Sequence b has lengths[b] keys in all; with
+    ``append`` the cache holds the first lengths[b] - 1 and the last one is
+    the new token (k_new, v_new), otherwise the cache holds all of them.
+    Lengths, Q, K and V are drawn exactly as gen_decode draws them (same
+    seed, same values).  The pool has sum(ceil(len / page_size)) +
+    spare_pages pages; their order is a random permutation from a second
+    generator seeded with seed + 7919, each sequence taking the next
+    ceil(len / page_size) of it.  Rows of a page past a sequence's cached
+    rows, and spare pages, are zero.
+    -> q [B,1,Hq,d], k_pages, v_pages [num_pages,page_size,Hkv,d],
+       block_table int32 [B,max_pages], cache_seqlens int32 [B],
+       k_new, v_new [B,1,Hkv,d] (None without append), lengths int64 [B]."""
+    gen = torch.Generator().manual_seed(seed)
+    if lengths is None:
+        lengths = gen_lengths(gen, B, lo, hi)
+    else:
+        lengths = torch.as_tensor(lengths, dtype=torch.int64)
+    t = DTYPES[dtype]
+    need = [-(-int(n) // page_size) for n in lengths]
+    max_pages = max(max(need), 1)
+    num_pages = sum(need) + spare_pages
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(seed + 7919))
+    table = torch.zeros((B, max_pages), dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[nxt:nxt + need[b]].to(torch.int32)
+        nxt += need[b]
+    cached = lengths - 1 if append else lengths
+    q = _normal(gen, (B, 1, Hq, d), sigma, t)
+    pools, new = {}, {}
+    for w in ("k", "v"):
+        pool = torch.zeros((num_pages, page_size, Hkv, d), dtype=t)
+        last = torch.zeros((B, 1, Hkv, d), dtype=t)
+        for b in range(B):
+            L, n_cached = int(lengths[b]), int(cached[b])
+            rows = _normal(gen, (L, Hkv, d), sigma, t)
+            if L > 0:
+                last[b, 0] = rows[L - 1]
+            for pg in range(need[b]):
+                a, e = pg * page_size, min((pg + 1) * page_size, n_cached)
+                if e > a:
+                    pool[int(table[b, pg]), :e - a] = rows[a:e]
+        pools[w], new[w] = pool, last
+    k_new, v_new = (new["k"], new["v"]) if append else (None, None)
+    return (q, pools["k"], pools["v"], table, cached.to(torch.int32), k_new, v_new, lengths)
+
+
 def generate(w: Workload):
     """Inputs of a named workload (CPU tensors)."""
     if w.kind == "fwd":

@@ -1,6 +1,7 @@
 /*
  * fa.h -- C ABI of the fused exact-attention library for MI355X (gfx950):
- * forward, KV-cache decode and the training backward.  Link against
+ * forward, KV-cache decode (contiguous or paged, with append) and the
+ * training backward.  Link against
  * libfa355.so.
  *
  * What is computed (all entry points): exact scaled-dot-product attention
@@ -135,6 +136,47 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
                               float softmax_scale, int split_size,
                               void* workspace, size_t workspace_bytes,
                               fa_dtype_t dtype, hipStream_t stream);
+
+/* One-token decode against a PAGED KV cache, optionally appending the new
+ * token's key and value first ("FlashAttention" project summary, feature
+ * list: the cached-decode call with paged KV cache support; explainer page,
+ * advice on generation with a cache: paged cache layouts cut waste; step 9
+ * for the split and combine).  The pages fix no layout; this one is:
+ *   k_pages, v_pages : [num_pages, page_size, Hkv, d], a pool of pages shared
+ *                      by all sequences; token t of sequence b is row
+ *                      t % page_size of page block_table[b][t / page_size]
+ *   block_table      : int32 [B, max_pages_per_seq] DEVICE array of page
+ *                      indices in [0, num_pages); entries past a sequence's
+ *                      last page are never read
+ *   cache_seqlens    : int32 [B] DEVICE array, tokens already in the cache
+ *   k_new, v_new     : [B, 1, Hkv, d] or both NULL.  When given, row b is
+ *                      written into the cache at position cache_seqlens[b]
+ *                      (k_pages, v_pages are modified), then the query
+ *                      attends over cache_seqlens[b] + 1 keys; when NULL it
+ *                      attends over cache_seqlens[b] keys (as
+ *                      fa_decode_kvcache, which includes the current token)
+ *   q, out, lse      : as for fa_decode_kvcache
+ *   page_size        : a positive multiple of 32
+ *   max_seqlen_k     : host upper bound of the keys attended (including an
+ *                      appended one), 1 <= max_seqlen_k <= max_pages_per_seq
+ *                      * page_size; the device clamps cache_seqlens to
+ *                      [0, max_seqlen_k] (with an append: to
+ *                      [0, max_seqlen_k - 1], the new row going there)
+ *   workspace        : at least fa_decode_workspace_bytes(B, Hq, max_seqlen_k,
+ *                      d, split_size) bytes, as for fa_decode_kvcache.
+ * Not checked (device data): table entries; an entry outside [0, num_pages)
+ * reads as zero keys and receives no appended row.  Three kernels are
+ * enqueued with an append (append, split, combine), two without.  Two calls
+ * that append into the same page rows race unless ordered by the caller. */
+fa_status_t fa_decode_paged(const void* q, void* k_pages, void* v_pages,
+                            const int32_t* block_table, const int32_t* cache_seqlens,
+                            const void* k_new, const void* v_new, void* out, float* lse,
+                            int B, int Hq, int Hkv, int num_pages, int page_size,
+                            int max_pages_per_seq, int max_seqlen_k, int d,
+                            int causal, int window_left, int window_right,
+                            float softmax_scale, int split_size,
+                            void* workspace, size_t workspace_bytes,
+                            fa_dtype_t dtype, hipStream_t stream);
 
 /* Bytes of fp32 workspace fa_bwd needs: one value per query row and head
  * (D_i = dO_i . O_i). */

@@ -33,8 +33,9 @@ def declared_functions():
 
 def test_header_declares_expected_api():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes",
-                                           "fa_decode_kvcache", "fa_bwd_workspace_bytes", "fa_bwd",
-                                           "fa_status_str", "fa_last_error"])
+                                           "fa_decode_kvcache", "fa_decode_paged",
+                                           "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+                                           "fa_last_error"])
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -125,6 +126,33 @@ def test_decode_rejects(lib, kw, status):
 def test_workspace_exact_boundary(lib):
     need = lib.fa_decode_workspace_bytes(2, 8, 4096, 128, 1024)
     assert decode(lib, ws_bytes=need - 1) == 3
+    assert "workspace too small" in lib.fa_last_error().decode()
+
+
+def paged(lib, kp=FAKE, table=FAKE, seqlens=FAKE, kn=None, vn=None, ws=FAKE, ws_bytes=1 << 30,
+          B=2, Hq=8, Hkv=2, num_pages=16, page=256, max_pages=8, maxk=2048, d=128, split=1024,
+          dtype=0):
+    return lib.fa_decode_paged(FAKE, kp, FAKE, table, seqlens, kn, vn, FAKE, FAKE, B, Hq, Hkv,
+                               num_pages, page, max_pages, maxk, d, 1, -1, -1, 0.1, split, ws,
+                               ws_bytes, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kp=None), 1), (dict(table=None), 1), (dict(table=FAKE + 2), 1), (dict(seqlens=None), 1),
+    (dict(kn=FAKE), 1), (dict(vn=FAKE), 1), (dict(kn=FAKE + 8, vn=FAKE), 1),
+    (dict(page=16), 1), (dict(page=48), 1), (dict(page=0), 1), (dict(num_pages=0), 1),
+    (dict(max_pages=0), 1), (dict(maxk=0), 1), (dict(maxk=8 * 256 + 1), 1), (dict(split=32), 1),
+    (dict(ws=None), 3), (dict(ws_bytes=1000), 3), (dict(d=96), 2), (dict(dtype=2), 2),
+    (dict(Hq=7), 1),
+])
+def test_paged_rejects(lib, kw, status):
+    assert paged(lib, **kw) == status
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_paged_workspace_exact_boundary(lib):
+    need = lib.fa_decode_workspace_bytes(2, 8, 2048, 128, 1024)
+    assert paged(lib, ws_bytes=need - 1) == 3
     assert "workspace too small" in lib.fa_last_error().decode()
 
 
