@@ -156,6 +156,87 @@ int fa_oracle_fwd(const double* q, const double* k, const double* v, double* out
     return err;
 }
 
+/* Score modifiers.  The "FlashAttention" explainer page, "Variants you may
+ * meet": ALiBi-style and relative-position biases add a term to the scores,
+ * and soft-capping of the scores needs explicit support in the kernel; the
+ * project summary lists ALiBi among the supported features.  The pages give
+ * no formulas; the readings used here are those of the fast library's
+ * forward arguments (alibi_slopes, softcap):
+ *   s_ij = scale * q_i . k_j
+ *   s_ij <- cap * tanh(s_ij / cap)                 if cap > 0 (soft-capping)
+ *   s_ij <- s_ij - slope_h * |pos_i - j|           (ALiBi, slope of query head h)
+ * with pos_i = i + (sk - sq) as for the masks; the softmax, O and LSE then
+ * follow the plain definition over the modified scores.  This row routine is
+ * a separate copy of attend_row so that the unmodified definition stays
+ * exactly as written above. */
+static void attend_row_mod(const double* qrow, const double* k, const double* v,
+                           long kv_stride, long i, long sq, long sk, int d,
+                           int causal, int wl, int wr, double scale, double softcap,
+                           double slope, double* orow, double* lse, double* scores)
+{
+    long pos = i + sk - sq; /* key-axis position of query row i */
+    double m = -INFINITY;
+    for (long j = 0; j < sk; ++j) {
+        if (!visible(i, j, sq, sk, causal, wl, wr)) continue;
+        double s = scale * dot(qrow, k + j * kv_stride, d);
+        if (softcap > 0) s = softcap * tanh(s / softcap);
+        s -= slope * fabs((double)(pos - j));
+        scores[j] = s;
+        if (s > m) m = s;
+    }
+    for (int t = 0; t < d; ++t) orow[t] = 0.0;
+    if (m == -INFINITY) {
+        *lse = -INFINITY;
+        return;
+    }
+    double l = 0.0;
+    for (long j = 0; j < sk; ++j)
+        if (visible(i, j, sq, sk, causal, wl, wr)) l += exp(scores[j] - m);
+    for (long j = 0; j < sk; ++j) {
+        if (!visible(i, j, sq, sk, causal, wl, wr)) continue;
+        double p = exp(scores[j] - m) / l;
+        for (int t = 0; t < d; ++t) orow[t] += p * v[j * kv_stride + t];
+    }
+    *lse = m + log(l);
+}
+
+/* Padded batch with score modifiers: as fa_oracle_fwd, plus softcap (0 =
+ * off) and alibi ([Hq] slopes, or NULL = no bias). */
+int fa_oracle_fwd_mod(const double* q, const double* k, const double* v,
+                      double* out, double* lse,
+                      int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                      int causal, int wl, int wr, double scale,
+                      double softcap, const double* alibi)
+{
+    if (Hkv <= 0 || Hq % Hkv != 0) return -2;
+    int G = Hq / Hkv;
+    int err = 0;
+#pragma omp parallel
+    {
+        double* scores = (double*)malloc(sizeof(double) * (size_t)(Sk > 0 ? Sk : 1));
+        if (!scores) {
+#pragma omp atomic write
+            err = -1;
+        } else {
+#pragma omp for collapse(3) schedule(dynamic, 16)
+            for (int b = 0; b < B; ++b)
+                for (int h = 0; h < Hq; ++h)
+                    for (int i = 0; i < Sq; ++i) {
+                        int g = h / G;
+                        double slope = alibi ? alibi[h] : 0.0;
+                        attend_row_mod(q + (((long)b * Sq + i) * Hq + h) * d,
+                                       k + ((long)b * Sk * Hkv + g) * d,
+                                       v + ((long)b * Sk * Hkv + g) * d, (long)Hkv * d,
+                                       i, Sq, Sk, d, causal, wl, wr, scale, softcap, slope,
+                                       out + (((long)b * Sq + i) * Hq + h) * d,
+                                       lse + ((long)b * Hq + h) * Sq + i, scores);
+                    }
+            free(scores);
+        }
+    }
+    return err;
+}
+
 /* Packed sequences. q,out: [total_q,Hq,d]; k,v: [total_k,Hkv,d];
  * lse: [Hq,total_q]; sequence z owns query rows [cu_q[z], cu_q[z+1]) and
  * key rows [cu_k[z], cu_k[z+1]). */

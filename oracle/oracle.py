@@ -57,8 +57,11 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                   i32, i32, i32, f64]
     lib.fa_oracle_decode_paged.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32,
                                            i32, i32, i32, i32, i32, i32, f64]
+    lib.fa_oracle_fwd_mod.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32,
+                                      i32, i32, i32, f64, f64, P]
     for f in (lib.fa_oracle_rows, lib.fa_oracle_fwd, lib.fa_oracle_varlen,
-              lib.fa_oracle_decode, lib.fa_oracle_bwd, lib.fa_oracle_decode_paged):
+              lib.fa_oracle_decode, lib.fa_oracle_bwd, lib.fa_oracle_decode_paged,
+              lib.fa_oracle_fwd_mod):
         f.restype = ctypes.c_int
     return lib
 
@@ -130,6 +133,29 @@ class Oracle:
                                     int(window[0]), int(window[1]), _scale(scale, d))
         if rc != 0:
             raise RuntimeError(f"oracle fwd failed: {rc}")
+        return out, lse
+
+    # -- padded batch with score modifiers ------------------------------------
+    def attention_mod(self, q, k, v, causal=False, window=(-1, -1), scale=None, softcap=0.0,
+                      alibi_slopes=None):
+        """As attention(), with soft-capping (cap * tanh(s / cap), 0 = off) and
+        an ALiBi bias -slope_h * |pos_i - j| (alibi_slopes: [Hq] or None)."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        B, Sq, Hq, d = q.shape
+        Bk, Sk, Hkv, dk = k.shape
+        assert Bk == B and dk == d and v.shape == k.shape
+        sl = None
+        if alibi_slopes is not None:
+            sl = _f64(alibi_slopes).reshape(-1)
+            assert sl.shape == (Hq,)
+        out = np.empty_like(q)
+        lse = np.empty((B, Hq, Sq), dtype=np.float64)
+        rc = self.lib.fa_oracle_fwd_mod(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        B, Hq, Hkv, Sq, Sk, d, int(bool(causal)),
+                                        int(window[0]), int(window[1]), _scale(scale, d),
+                                        float(softcap), _ptr(sl) if sl is not None else None)
+        if rc != 0:
+            raise RuntimeError(f"oracle fwd_mod failed: {rc}")
         return out, lse
 
     # -- gradients (padded batch) -------------------------------------------
@@ -256,6 +282,10 @@ def default() -> Oracle:
 
 def attention(*a, **kw):
     return default().attention(*a, **kw)
+
+
+def attention_mod(*a, **kw):
+    return default().attention_mod(*a, **kw)
 
 
 def attention_varlen(*a, **kw):

@@ -642,6 +642,99 @@ def pin_paged_append_zero_query(orc):
             assert np.abs(out[b, 0, h] - mean).max() < 1e-13
 
 
+_MOD_CASES = [  # Sq, Sk, causal, wl, wr, softcap, with ALiBi
+    (6, 6, False, -1, -1, 0.0, True), (6, 6, True, -1, -1, 0.0, True), (5, 9, True, -1, -1, 0.0, True),
+    (9, 5, False, 2, 1, 0.0, True), (6, 6, True, -1, -1, 1.5, False), (7, 7, False, -1, -1, 2.0, False),
+    (8, 8, True, 3, -1, 1.2, True), (4, 10, False, -1, -1, 0.7, True),
+]
+
+
+def _mod_reference(q, k, v, causal, wl, wr, scale, softcap, slopes):
+    """torch float64: scores, soft-capping, ALiBi bias from explicit
+    positions, mask, softmax, logsumexp, all written out independently."""
+    B, Sq, Hq, d = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(G, dim=1)
+    s = scale * torch.matmul(qt, kt.transpose(-1, -2))
+    if softcap > 0:
+        s = softcap * torch.tanh(s / softcap)
+    if slopes is not None:
+        qpos = torch.arange(Sq, dtype=torch.float64)[:, None] + (Sk - Sq)
+        kpos = torch.arange(Sk, dtype=torch.float64)[None, :]
+        s = s - torch.from_numpy(slopes)[:, None, None] * (qpos - kpos).abs()
+    vis = _visible_band(Sq, Sk, causal, wl, wr)
+    s = s.masked_fill(~vis, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    w = torch.softmax(s, dim=-1).nan_to_num(0.0)
+    o = torch.matmul(w, vt).permute(0, 2, 1, 3)
+    return o.numpy(), lse.numpy()
+
+
+def pin_mod_torch_reference(orc):
+    """Soft-capping and ALiBi against an independent torch float64 version
+    (every mask mode, Sq != Sk alignment, GQA)."""
+    rng = _rng(70)
+    B, Hq, Hkv, d, scale = 2, 4, 2, 6, 0.8
+    for (Sq, Sk, causal, wl, wr, cap, alibi) in _MOD_CASES:
+        q = 2 * _rand(rng, B, Sq, Hq, d); k = _rand(rng, B, Sk, Hkv, d); v = _rand(rng, B, Sk, Hkv, d)
+        slopes = np.array([0.5, 0.25, 0.125, 0.0625]) if alibi else None
+        o1, l1 = orc.attention_mod(q, k, v, causal=causal, window=(wl, wr), scale=scale,
+                                   softcap=cap, alibi_slopes=slopes)
+        o2, l2 = _mod_reference(q, k, v, causal, wl, wr, scale, cap, slopes)
+        fin = np.isfinite(l2)
+        assert np.array_equal(np.isfinite(l1), fin)
+        assert np.abs(o1 - o2).max() < 1e-12 and np.abs(l1[fin] - l2[fin]).max() < 1e-12
+
+
+def pin_mod_neutral(orc):
+    """No cap and zero (or no) slopes give the plain definition exactly."""
+    rng = _rng(71)
+    q = _rand(rng, 1, 7, 4, 5); k = _rand(rng, 1, 9, 2, 5); v = _rand(rng, 1, 9, 2, 5)
+    for causal in (False, True):
+        o0, l0 = orc.attention(q, k, v, causal=causal, scale=0.6)
+        for slopes in (None, np.zeros(4)):
+            o1, l1 = orc.attention_mod(q, k, v, causal=causal, scale=0.6, alibi_slopes=slopes)
+            assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def pin_alibi_zero_query_closed_form(orc):
+    """Q = 0: scores are -slope * distance, so LSE_i is the log of a sum of
+    two geometric series (keys at or before the row, keys after it)."""
+    n, slope = 9, 0.3
+    rng = _rng(72)
+    k = _rand(rng, 1, n, 1, 4); v = _rand(rng, 1, n, 1, 4)
+    r = math.exp(-slope)
+    for causal in (True, False):
+        _, lse = orc.attention_mod(np.zeros((1, n, 1, 4)), k, v, causal=causal,
+                                   alibi_slopes=np.array([slope]))
+        for i in range(n):
+            before = (1 - r ** (i + 1)) / (1 - r)
+            after = 0.0 if causal else r * (1 - r ** (n - 1 - i)) / (1 - r)
+            assert abs(lse[0, 0, i] - math.log(before + after)) < 1e-13
+
+
+def pin_softcap_saturates(orc):
+    """Scores of +-1e6 capped at 5 become +-5: two keys give weights
+    e^5 / (e^5 + e^-5) and LSE = ln(e^5 + e^-5); a huge cap is the plain
+    definition."""
+    d = 2
+    q = np.array([[[[1000.0, 0.0]]]])
+    k = np.array([[[[1000.0, 0.0]], [[-1000.0, 0.0]]]])
+    v = np.array([[[[1.0, 0.0]], [[0.0, 1.0]]]])
+    o, lse = orc.attention_mod(q, k, v, scale=1.0, softcap=5.0)
+    w = math.exp(5) / (math.exp(5) + math.exp(-5))
+    assert abs(lse[0, 0, 0] - math.log(math.exp(5) + math.exp(-5))) < 1e-13
+    assert abs(o[0, 0, 0, 0] - w) < 1e-13 and abs(o[0, 0, 0, 1] - (1 - w)) < 1e-13
+    rng = _rng(73)
+    q = _rand(rng, 1, 5, 2, d); k = _rand(rng, 1, 6, 2, d); v = _rand(rng, 1, 6, 2, d)
+    o0, l0 = orc.attention(q, k, v, causal=True, scale=0.5)
+    o1, l1 = orc.attention_mod(q, k, v, causal=True, scale=0.5, softcap=1e7)
+    assert np.abs(o0 - o1).max() < 1e-10 and np.abs(l0 - l1).max() < 1e-10
+
+
 PINS = [
     pin_worked_example, pin_torch_sdpa, pin_zero_query_closed_form, pin_varlen_zero_query,
     pin_decode_zero_query, pin_constant_v, pin_single_visible_key, pin_one_hot_values,
@@ -650,5 +743,6 @@ PINS = [
     pin_split_combine, pin_fully_masked_rows, pin_large_scores_stable, pin_mpmath_brute_force,
     pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_identities,
     pin_bwd_gqa_equals_repeated_mha, pin_paged_equals_contiguous, pin_paged_append,
-    pin_paged_append_zero_query,
+    pin_paged_append_zero_query, pin_mod_torch_reference, pin_mod_neutral,
+    pin_alibi_zero_query_closed_form, pin_softcap_saturates,
 ]

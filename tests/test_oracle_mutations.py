@@ -63,6 +63,13 @@ MUTANTS = {
     "append_not_seen": ("long sk = (long)cache_seqlens[b] + append;", "long sk = (long)cache_seqlens[b];"),
     "append_value_from_key": ("v_pages[(row * Hkv + g) * d + c] = v_new[((long)b * Hkv + g) * d + c];",
                               "v_pages[(row * Hkv + g) * d + c] = k_new[((long)b * Hkv + g) * d + c];"),
+    "alibi_sign_flipped": ("s -= slope * fabs((double)(pos - j));", "s += slope * fabs((double)(pos - j));"),
+    "alibi_without_abs": ("s -= slope * fabs((double)(pos - j));", "s -= slope * (double)(pos - j);"),
+    "alibi_kv_head_slope": ("double slope = alibi ? alibi[h] : 0.0;", "double slope = alibi ? alibi[g] : 0.0;"),
+    "alibi_top_left": ("long pos = i + sk - sq;", "long pos = i;"),
+    "softcap_not_divided": ("if (softcap > 0) s = softcap * tanh(s / softcap);",
+                            "if (softcap > 0) s = softcap * tanh(s);"),
+    "softcap_ignored": ("if (softcap > 0) s = softcap * tanh(s / softcap);", "if (softcap > 0) s = s;"),
     "append_head_ignored": ("k_pages[(row * Hkv + g) * d + c] = k_new[((long)b * Hkv + g) * d + c];",
                             "k_pages[(row * Hkv + g) * d + c] = k_new[((long)b * Hkv) * d + c];"),
 }
