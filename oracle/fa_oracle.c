@@ -189,15 +189,15 @@ static void attend_row_mod(const double* qrow, const double* k, const double* v,
         *lse = -INFINITY;
         return;
     }
-    double l = 0.0;
+    double sum = 0.0;
     for (long j = 0; j < sk; ++j)
-        if (visible(i, j, sq, sk, causal, wl, wr)) l += exp(scores[j] - m);
+        if (visible(i, j, sq, sk, causal, wl, wr)) sum += exp(scores[j] - m);
     for (long j = 0; j < sk; ++j) {
         if (!visible(i, j, sq, sk, causal, wl, wr)) continue;
-        double p = exp(scores[j] - m) / l;
+        double p = exp(scores[j] - m) / sum;
         for (int t = 0; t < d; ++t) orow[t] += p * v[j * kv_stride + t];
     }
-    *lse = m + log(l);
+    *lse = m + log(sum);
 }
 
 /* Padded batch with score modifiers: as fa_oracle_fwd, plus softcap (0 =
