@@ -7,7 +7,8 @@ KV-cache decode workload (B=64, Hq=32, Hkv=8, d=128, cache lengths
 U{1024..32768}, split 1024 + combine) is timed beside it and reported under
 "decode"; the same keys in a shuffled pool of 256-row pages, with each
 sequence's last key appended by the call (fa_decode_paged: append, split,
-combine), under "decode_paged"; and the backward (fa_bwd, three kernels) of
+combine), under "decode_paged"; the prefill with ALiBi and/or soft-capping
+(fa_fwd_mod) under "forward_modifiers"; and the backward (fa_bwd, three kernels) of
 the prefill workload under "backward".  Inputs are seeded synthetic tensors already resident in
 HBM.
 
@@ -89,7 +90,7 @@ def _timed(fn, steps: int, warmup: int):
     return wall, e0.elapsed_time(e1) / steps
 
 
-def bench_prefill(steps, warmup, w):
+def bench_prefill(steps, warmup, w, with_mods=False):
     q, k, v = synth.generate(w)
     dev = "cuda:0"
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -101,7 +102,37 @@ def bench_prefill(steps, warmup, w):
         fa.fwd(qd, kd, vd, causal=w.causal, window=w.window, out=out, lse=lse)
 
     wall, ev = _timed(step, steps, warmup)
-    return q, k, v, work, wall, ev
+    mods = None
+    if with_mods:
+        ms, mw = max(5, steps // 4), max(2, warmup // 4)
+        mods = [bench_fwd_mod(ms, mw, w, qd, kd, vd, 0.0, True),
+                bench_fwd_mod(ms, mw, w, qd, kd, vd, 50.0, False),
+                bench_fwd_mod(ms, mw, w, qd, kd, vd, 50.0, True)]
+    return q, k, v, work, wall, ev, mods
+
+
+def bench_fwd_mod(steps, warmup, w, qd, kd, vd, softcap, alibi):
+    """fa_fwd_mod on the prefill workload's resident inputs: ALiBi (the usual
+    geometric slopes 2^(-8 (h+1) / Hq)) and/or soft-capping.  FLOP as the
+    plain forward (the modifier arithmetic is not counted)."""
+    slopes = None
+    if alibi:
+        slopes = torch.tensor([2.0 ** (-8.0 * (h + 1) / w.Hq) for h in range(w.Hq)],
+                              dtype=torch.float32, device=qd.device)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=qd.device)
+    work = metrics.fwd_work(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window)
+
+    def step():
+        fa.fwd_mod(qd, kd, vd, causal=w.causal, window=w.window, alibi_slopes=slopes,
+                   softcap=softcap, out=out, lse=lse)
+
+    wall, ev = _timed(step, steps, warmup)
+    tf = work["flop"] / (ev * 1e-3) / 1e12
+    name = "+".join(x for x, on in (("alibi", alibi), (f"softcap{softcap:g}", softcap > 0)) if on)
+    return {"workload": f"{w.name}_{name}", "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(wall, 4), "event_ms_per_call": round(ev, 4),
+            "frac_bf16_mfma_peak": round(tf / metrics.PEAK_BF16_TFLOPS, 4)}
 
 
 def bench_decode(steps, warmup):
@@ -233,6 +264,7 @@ def main():
                     choices=[n for n, w in synth.WORKLOADS.items() if w.kind == "fwd"])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-mods", action="store_true", help="skip the score-modifier legs")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -251,7 +283,8 @@ def main():
     fa.load()   # fails loudly if the HIP library is not built
 
     w = synth.WORKLOADS[args.workload]
-    q, k, v, work, wall, ev = bench_prefill(args.steps, args.warmup, w)
+    q, k, v, work, wall, ev, mods = bench_prefill(args.steps, args.warmup, w,
+                                                  with_mods=not args.no_mods)
     tflops_wall = work["flop"] / (wall * 1e-3) / 1e12
     tflops_ev = work["flop"] / (ev * 1e-3) / 1e12
     line = {
@@ -277,6 +310,8 @@ def main():
                      "avg_launch_ms": round(ev, 5),
                      "traffic": profiled_traffic(f"fa_fwd_kernel_{w.name}.md", "fa_fwd.hip")},
     }
+    if mods is not None:
+        line["forward_modifiers"] = mods
     if not args.no_decode:
         del q
         line["decode"] = bench_decode(max(10, args.steps // 2), max(3, args.warmup // 2))

@@ -118,6 +118,50 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
 }
 
+fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                       int window_right, float softmax_scale, const float* alibi_slopes,
+                       float softcap, fa_dtype_t dtype, hipStream_t stream) {
+    if (alibi_slopes && !aligned4(alibi_slopes))
+        return fail(FA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
+    if (!std::isfinite(softcap) || softcap < 0.f)
+        return fail(FA_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0 = off)");
+    if (!alibi_slopes && softcap == 0.f)
+        return fa_fwd(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, d, causal, window_left, window_right,
+                      softmax_scale, dtype, stream);
+    fa_status_t st = check_common(q, k, v, out, lse, B, Hq, Hkv, d, window_left, window_right,
+                                  softmax_scale, dtype, Sk == 0);
+    if (st != FA_OK) return st;
+    if (Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARG, "Sq, Sk must be >= 0 (got %d, %d)", Sq, Sk);
+    if (Sq == 0) return ok();
+    if ((st = check_seq_bytes(Sq, Hq, d, "q")) != FA_OK) return st;
+    if ((st = check_seq_bytes(Sk, Hkv, d, "k/v")) != FA_OK) return st;
+    fa::FwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
+    p.cu_q = nullptr; p.cu_k = nullptr;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sq = Sq; p.Sk = Sk;
+    p.gw = fa::fwd_heads_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.nqt = (Sq + p.bm - 1) / p.bm;
+    p.q_tok_stride = (long long)Hq * d;
+    p.kv_tok_stride = (long long)Hkv * d;
+    p.lse_b_stride = (long long)Hq * Sq;
+    p.lse_h_stride = Sq;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    set_scale(softmax_scale, &p.c, &p.qsign);
+    p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
+    p.mod = (alibi_slopes ? 1 : 0) | (softcap > 0.f ? 2 : 0);
+    p.alibi = alibi_slopes;
+    if (softcap > 0.f) {
+        p.sc_k = 2.f * std::fabs(softmax_scale) * fa::kLog2e_host / softcap;
+        p.sc_c = softcap * fa::kLog2e_host;
+    }
+    if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
+}
+
 fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int Hq,
                           int Hkv, int max_seqlen_q, int max_seqlen_k, int total_q, int d,

@@ -119,7 +119,14 @@ __device__ __forceinline__ u32x4 in_acc_regs(u32x4 v) {
     return r;
 }
 
-template <int D, bool BF16, bool VARLEN>
+// MOD selects the score modifiers (bit 0: ALiBi, bit 1: soft-capping): the
+// explainer page's "Variants you may meet" (a bias term added to the scores;
+// capped scores need explicit kernel support).  With them the exponent of
+// score s of key j in row i (log2 units, before the running max) is
+//     u = cap log2(e) tanh(scale s / cap) - slope log2(e) |pos_i - j|
+// (each part only when enabled); tanh(y) = 1 - 2 / (exp2(2 y log2 e) + 1).
+// MOD = 0 compiles to the unmodified kernel.
+template <int D, bool BF16, bool VARLEN, int MOD>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_kernel(FwdParams p) {
     using T = FwdGeo<D>;
@@ -163,6 +170,7 @@ void fa_fwd_kernel(FwdParams p) {
     }
     const int hq = hg * gw + wave % gw;
     const int hkv = hq / p.G;
+    constexpr bool ALIBI = (MOD & 1) != 0, SOFTCAP = (MOD & 2) != 0;
 
     long long q_tok0, k_tok0;
     int sq, sk;
@@ -344,8 +352,14 @@ void fa_fwd_kernel(FwdParams p) {
         if (wr >= 0) hh = min(hh, pos + wr);
         rel_hi[h] = hh - 4 * g;
     }
+    // ALiBi: slope in log2 units; element e of tile jt of half h lies at
+    // signed distance 4g - lq - (r0[h] + delta) + 32 jt + 8 (e / 4) + e % 4
+    // from its row
+    const float slope2 = ALIBI ? p.alibi[hq] * kLog2e : 0.f;
+    const float sc_k = p.sc_k, sc_c = p.sc_c;
 
     f32x16 sacc[2];                            // S^T of each half
+    int js[2] = {0, 0};                        // key tile of each half's S (for ALiBi)
     u32x4 pb[2][T::KK];                        // P of each half as 16-bit B operands
     u32x4 kbuf[2][T::KS];                      // K operands, by step parity
     u32x4 vbuf[2][T::KK][T::DB];               // V operands, by step parity
@@ -385,11 +399,35 @@ void fa_fwd_kernel(FwdParams p) {
     // key reproduces that key's V row), LSE by the sum of the fp32 values
     // (16-bit rounding would bias it by up to 2^-9).  Both are summed as
     // trees: with one wave per SIMD a chain of dependent adds stalls.
+    // exp2 argument of element e of half h with running max m; tb is the
+    // distance of the half's tile's element 0 (ALiBi only)
+    auto earg = [&](int h, int e, float tb, float m) __attribute__((always_inline)) {
+        const float s = sacc[h][e];
+        if constexpr (MOD == 0) {
+            return fmaf(s, c, -m);
+        } else {
+            float v;
+            if constexpr (SOFTCAP) {
+                const float ex = exp2_fast(s * sc_k);
+                const float th = fmaf(-2.f, __builtin_amdgcn_rcpf(ex + 1.f), 1.f);
+                v = s == -INFINITY ? -INFINITY : fmaf(th, sc_c, -m);   // masked stays masked
+            } else {
+                v = fmaf(s, c, -m);
+            }
+            if constexpr (ALIBI)
+                v = fmaf(-slope2, fabsf(tb + (float)(8 * (e >> 2) + (e & 3))), v);
+            return v;
+        }
+    };
+    auto tile_base = [&](int h) __attribute__((always_inline)) {
+        return ALIBI ? (float)(4 * g - lq + (js[h] * T::BN - r0[h] - delta)) : 0.f;
+    };
     auto exps_plain = [&](int h) __attribute__((always_inline)) {
         const float m_use = m_run[h] == -INFINITY ? 0.f : m_run[h];
+        const float tb = tile_base(h);
         float x[16], r2[2] = {0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = exp2_fast(fmaf(sacc[h][e], c, -m_use));
+        for (int e = 0; e < 16; ++e) x[e] = exp2_fast(earg(h, e, tb, m_use));
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
@@ -404,13 +442,20 @@ void fa_fwd_kernel(FwdParams p) {
     };
     auto refresh = [&](int h) __attribute__((always_inline)) {
         asm volatile("");   // keep this rare block a real branch (not speculated)
-        f32x16& s = sacc[h];
+        f32x16 s;
+        if constexpr (MOD == 0) {
+            s = sacc[h];
+        } else {
+            const float tb = tile_base(h);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = earg(h, e, tb, 0.f);   // u, log2 units
+        }
         float m4[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
             m4[q4] = fmaxf(fmaxf(s[4 * q4], s[4 * q4 + 1]), fmaxf(s[4 * q4 + 2], s[4 * q4 + 3]));
         const float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-        const float mnew = fmaxf(m_run[h], mx * c);          // -inf stays -inf (c > 0)
+        const float mnew = fmaxf(m_run[h], MOD == 0 ? mx * c : mx);   // -inf stays -inf (c > 0)
         const bool raise = mnew > m_run[h] + kRescaleThreshold;
         const float alpha = raise ? exp2_fast(m_run[h] - mnew) : 1.f;
         l_run[h] *= alpha;
@@ -465,14 +510,16 @@ void fa_fwd_kernel(FwdParams p) {
     // the same region.  sched_barrier(0) fences keep the order: with one
     // wave per SIMD the matrix and vector pipes only overlap as far as the
     // instruction stream alternates them.
-    auto fast_region = [&](auto hsc, const u32x4 (&kq)[T::KS], const u32x4 (&vq)[T::KK][T::DB],
-                           auto&& load) __attribute__((always_inline)) {
+    auto fast_region = [&](auto hsc, int jt, const u32x4 (&kq)[T::KS],
+                           const u32x4 (&vq)[T::KK][T::DB], auto&& load) __attribute__((always_inline)) {
         constexpr int hs = decltype(hsc)::value, hp = 1 - hs;
         constexpr int NS = T::KS + T::KK * T::DB;       // MFMA slots
         constexpr int EPS = 16 / NS;                    // exponentials per slot
         static_assert(EPS * NS == 16, "whole exponentials per slot");
         const bool first = m_run[hp] == -INFINITY;
         const float m_use = first ? 0.f : m_run[hp];
+        const float tb = tile_base(hp);
+        js[hs] = jt;
         float x[16], a[8], bsum[4], r2[2] = {0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
@@ -486,7 +533,7 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int j = 0; j < EPS; ++j) {
                 const int e = i * EPS + j;
-                x[e] = exp2_fast(fmaf(sacc[hp][e], c, -m_use));
+                x[e] = exp2_fast(earg(hp, e, tb, m_use));
             }
             // pair j (elements 2j, 2j+1) is packed and summed in the slot
             // after its second exponential; pairs of sums one slot later
@@ -536,12 +583,12 @@ void fa_fwd_kernel(FwdParams p) {
         constexpr int NQ = T::KK * T::DB;
         u32x4 kn[T::KS];
         u32x2 vlo[NQ], vhi[NQ];
-        fast_region(int_c<0>{}, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
+        fast_region(int_c<0>{}, jt, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
             if (i < T::KS) kn[i] = k_load(kt, i);
             else vlo[i - T::KS] = v_half(vt, i - T::KS, 0);
             if (i % CSTEP == CSTEP / 2) copy_one(sc, i / CSTEP);
         });
-        fast_region(int_c<1>{}, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
+        fast_region(int_c<1>{}, jt, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
             if (i < NQ) vhi[i] = v_half(vt, i, 1);
         });
 #pragma unroll
@@ -562,16 +609,52 @@ void fa_fwd_kernel(FwdParams p) {
             load_k_now(kslot(jt));
             qk(0, kbuf[0]);
             softmax_tile(1);
+            js[0] = jt;
             pv(0, vbuf[1]);
             apply_mask(0, jt);
             qk(1, kbuf[0]);
             softmax_tile(0);
+            js[1] = jt;
             pv(1, vbuf[1]);
             apply_mask(1, jt);
             load_v_now(vslot(jt));
         }
         if (!even) sync_pair();
     };
+
+    // ALiBi: the bias grows toward each row's own position, so in key order
+    // a row's running max would climb tile after tile (and take the rare
+    // path on most steps).  Instead the max starts at the row's largest
+    // modified score in the tile holding the half's last diagonal key,
+    // loaded straight from memory here: a value the row attains, so the
+    // running max never exceeds the true one and later tiles are scaled
+    // against it from the start.  (A zero slope keeps the plain order of
+    // maxima, hence the plain result bit for bit.)
+    if constexpr (ALIBI) {
+        if (ntiles > 0 && slope2 != 0.f) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (pw_lo[h] > pw_hi[h]) continue;              // uniform per wave
+                const int dt = min(max((r0[h] + T::HR - 1 + delta) / T::BN, pw_lo[h]), pw_hi[h]);
+                const auto krs = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(kseq + (long long)dt * (T::BN * tok_bytes_kv)), (short)0,
+                    min(sk - dt * T::BN, T::BN) * tok_bytes_kv, 0x00020000);
+                u32x4 kq[T::KS];
+#pragma unroll
+                for (int ks = 0; ks < T::KS; ++ks)
+                    kq[ks] = __builtin_amdgcn_raw_buffer_load_b128(
+                        krs, (lane & 31) * tok_bytes_kv + (2 * ks + g) * 16, 0, 0);
+                qk(h, kq);
+                apply_mask(h, dt);
+                js[h] = dt;
+                const float tb = tile_base(h);
+                float mx = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, earg(h, e, tb, 0.f));
+                m_run[h] = max_halves(mx);
+            }
+        }
+    }
 
     // Pipeline: step jt computes S_A(jt), S_B(jt) = K_jt Q^T; P_B(jt-1) and
     // P_A(jt); O_A and O_B += V_{jt-1} P(jt-1).  Before the first computed
@@ -656,22 +739,32 @@ void fa_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, bool BF16, bool VARLEN>
+template <int D, bool BF16, bool VARLEN, int MOD>
 static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
     const long long nblocks = (long long)p.nqt * (p.Hq / p.gw) * p.B;
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN, MOD>), dim3((unsigned)nblocks),
                        dim3(kFwdThreads), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStream_t s) {
-    if (d == 128) {
-        if (bf16) return varlen ? launch_one<128, true, true>(p, s) : launch_one<128, true, false>(p, s);
-        return varlen ? launch_one<128, false, true>(p, s) : launch_one<128, false, false>(p, s);
+template <int D, bool BF16>
+static hipError_t launch_mod(const FwdParams& p, hipStream_t s) {
+    switch (p.mod) {
+        case 1: return launch_one<D, BF16, false, 1>(p, s);
+        case 2: return launch_one<D, BF16, false, 2>(p, s);
+        case 3: return launch_one<D, BF16, false, 3>(p, s);
+        default: return launch_one<D, BF16, false, 0>(p, s);
     }
-    if (bf16) return varlen ? launch_one<64, true, true>(p, s) : launch_one<64, true, false>(p, s);
-    return varlen ? launch_one<64, false, true>(p, s) : launch_one<64, false, false>(p, s);
+}
+
+hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStream_t s) {
+    if (varlen) {
+        if (d == 128) return bf16 ? launch_one<128, true, true, 0>(p, s) : launch_one<128, false, true, 0>(p, s);
+        return bf16 ? launch_one<64, true, true, 0>(p, s) : launch_one<64, false, true, 0>(p, s);
+    }
+    if (d == 128) return bf16 ? launch_mod<128, true>(p, s) : launch_mod<128, false>(p, s);
+    return bf16 ? launch_mod<64, true>(p, s) : launch_mod<64, false>(p, s);
 }
 
 }  // namespace fa

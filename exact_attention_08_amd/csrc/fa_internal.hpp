@@ -29,6 +29,11 @@ struct FwdParams {
     int xcd_groups;             // (B*Hkv)/8 when B*Hkv % 8 == 0, else 0 (no remap)
     int gw;                     // query heads per work-group (fwd_heads_per_wg(G))
     int bm;                     // query rows per work-group (fwd_rows_per_wg(G))
+    // score modifiers (padded forward only)
+    int mod;                    // bit 0: ALiBi bias, bit 1: soft-capping
+    const float* alibi;         // [Hq] slopes (bias -slope * |pos - j|, natural-log units)
+    float sc_k;                 // soft-capping: 2 |scale| log2(e) / cap
+    float sc_c;                 // soft-capping: cap * log2(e)
 };
 
 // Decode split kernel + combine kernel.

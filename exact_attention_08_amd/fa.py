@@ -23,7 +23,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_E
           4: "FA_ERR_HIP"}
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
+EXPORTS = ("fa_fwd", "fa_fwd_mod", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
            "fa_decode_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
            "fa_last_error")
 
@@ -53,6 +53,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
         lib.fa_fwd.restype = I
+        lib.fa_fwd_mod.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, F, I, P]
+        lib.fa_fwd_mod.restype = I
         lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P]
         lib.fa_fwd_varlen.restype = I
         lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -122,6 +124,30 @@ def fwd(q, k, v, *, causal=False, window=(-1, -1), softmax_scale=None, out=None,
     _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                          int(bool(causal)), int(window[0]), int(window[1]),
                          _scale(softmax_scale, d), _DTYPE[q.dtype], _stream()))
+    return out, lse
+
+
+def fwd_mod(q, k, v, *, causal=False, window=(-1, -1), softmax_scale=None, alibi_slopes=None,
+            softcap=0.0, out=None, lse=None):
+    """fwd() with score modifiers: alibi_slopes (fp32 [Hq] GPU tensor, bias
+    -slope_h * |pos_i - j|) and softcap (cap * tanh(s / cap), 0 = off)."""
+    _check_tensors(q, k, v)
+    _require(q.dim() == 4 and k.dim() == 4 and k.shape == v.shape, "expected [B,S,H,d] q, k, v")
+    B, Sq, Hq, d = q.shape
+    _, Sk, Hkv, _ = k.shape
+    if alibi_slopes is not None:
+        _require(alibi_slopes.is_cuda and alibi_slopes.dtype == torch.float32
+                 and alibi_slopes.is_contiguous() and alibi_slopes.numel() == Hq,
+                 "alibi_slopes must be a contiguous fp32 [Hq] GPU tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    lib = load()
+    _check(lib.fa_fwd_mod(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                          int(bool(causal)), int(window[0]), int(window[1]),
+                          _scale(softmax_scale, d), _ptr(alibi_slopes), float(softcap),
+                          _DTYPE[q.dtype], _stream()))
     return out, lse
 
 

@@ -88,6 +88,26 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
                    int causal, int window_left, int window_right, float softmax_scale,
                    fa_dtype_t dtype, hipStream_t stream);
 
+/* Padded batch with score modifiers (the "FlashAttention" explainer page,
+ * "Variants you may meet": bias terms such as ALiBi added to the scores, and
+ * soft-capping of the scores, which needs kernel support; the project
+ * summary lists ALiBi).  The pages give no formulas; the scores are those of
+ * the fast library's alibi_slopes and softcap arguments:
+ *     s_ij = scale * q_i . k_j
+ *     s_ij = softcap * tanh(s_ij / softcap)        when softcap > 0
+ *     s_ij = s_ij - alibi_slopes[h] * |pos_i - j|   when alibi_slopes != NULL
+ * (pos_i as in the mask rule; h the query head), then softmax, O and LSE as
+ * above over the modified scores.
+ *   alibi_slopes : fp32 [Hq] DEVICE array, or NULL (no bias)
+ *   softcap      : finite, >= 0; 0 = off
+ * Other arguments, layouts and errors as fa_fwd; with no bias and no cap
+ * the call is fa_fwd. */
+fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                       int causal, int window_left, int window_right, float softmax_scale,
+                       const float* alibi_slopes, float softcap,
+                       fa_dtype_t dtype, hipStream_t stream);
+
 /* Packed sequences (flash_attn_varlen_func; "The One-Line Change ..." page,
  * sequence packing).  B sequences; sequence z owns query rows
  * [cu_seqlens_q[z], cu_seqlens_q[z+1]) and key rows

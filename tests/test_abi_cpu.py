@@ -32,7 +32,8 @@ def declared_functions():
 
 
 def test_header_declares_expected_api():
-    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_varlen", "fa_decode_workspace_bytes",
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_mod", "fa_fwd_varlen",
+                                           "fa_decode_workspace_bytes",
                                            "fa_decode_kvcache", "fa_decode_paged",
                                            "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                                            "fa_last_error"])
@@ -80,6 +81,30 @@ def test_fwd_empty_query_is_a_noop(lib):
     # Sq == 0 returns before any HIP call, with nothing enqueued
     assert fwd(lib, Sq=0) == 0
     assert lib.fa_last_error().decode() == ""
+
+
+def fwd_mod(lib, alibi=None, softcap=0.0, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128,
+             causal=0, wl=-1, wr=-1, scale=0.125, dtype=0)
+    a.update(kw)
+    return lib.fa_fwd_mod(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Sq"], a["Sk"], a["d"], a["causal"], a["wl"], a["wr"], a["scale"],
+                          alibi, softcap, a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(softcap=-1.0), 1), (dict(softcap=math.nan), 1), (dict(softcap=math.inf), 1),
+    (dict(alibi=FAKE + 2), 1), (dict(alibi=FAKE, q=None), 1), (dict(softcap=5.0, d=96), 2),
+    (dict(alibi=FAKE, Hq=6, Hkv=4), 1), (dict(softcap=2.0, scale=math.inf), 1),
+    (dict(q=None), 1),    # no modifier: the plain forward's checks
+])
+def test_fwd_mod_rejects(lib, kw, status):
+    assert fwd_mod(lib, **kw) == status
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_fwd_mod_empty_query_is_a_noop(lib):
+    assert fwd_mod(lib, alibi=FAKE, softcap=3.0, Sq=0) == 0
 
 
 def varlen(lib, cu_q=FAKE, cu_k=FAKE, B=2, maxq=8, maxk=8, total_q=10, d=128, **kw):
