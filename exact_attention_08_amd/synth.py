@@ -82,6 +82,27 @@ def gen_padded(seed: int, B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int,
     return q, k, v
 
 
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor 8-bit e4m3 quantisation of a float tensor: descale =
+    max|x| / 448 (the format's largest value), codes = RNE(x / descale) as
+    torch's float8_e4m3fn cast, returned as uint8 with the fp32 descale."""
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = amax / 448.0 if amax > 0 else 1.0
+    codes = (x.float() / descale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, float(torch.tensor(descale, dtype=torch.float32))
+
+
+def gen_fp8(seed: int, B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, sigma: float = 1.0):
+    """8-bit inputs: fp32 N(0, sigma^2) drawn as gen_padded draws them (Q, K,
+    V in that order), each tensor quantised per tensor by quantize_e4m3.
+    -> (q8, k8, v8) uint8 [B,S,H,d] and (descale_q, descale_k, descale_v)."""
+    gen = torch.Generator().manual_seed(seed)
+    xs = [_normal(gen, shape, sigma, torch.float32)
+          for shape in ((B, Sq, Hq, d), (B, Sk, Hkv, d), (B, Sk, Hkv, d))]
+    out = [quantize_e4m3(x) for x in xs]
+    return tuple(c for c, _ in out), tuple(s for _, s in out)
+
+
 def gen_grad(seed: int, shape, dtype: str = "bf16", sigma: float = 1.0) -> torch.Tensor:
     """A seeded incoming gradient (dL/dO) of the given shape, N(0, sigma^2)."""
     gen = torch.Generator().manual_seed(seed)

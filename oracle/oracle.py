@@ -113,6 +113,25 @@ def _scale(scale, d: int) -> float:
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def decode_e4m3(codes) -> np.ndarray:
+    """fp64 values of 8-bit e4m3 codes (the OCP 8-bit floating-point format:
+    1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+    holds the subnormals m/8 * 2^-6; no infinities; S.1111.111 is NaN)."""
+    try:
+        import torch
+        if isinstance(codes, torch.Tensor):
+            codes = codes.detach().to("cpu").view(torch.uint8).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.ascontiguousarray(sign * mag)
+
+
 class Oracle:
     """Thin marshalling wrapper around one loaded oracle shared object."""
 
@@ -157,6 +176,20 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"oracle fwd_mod failed: {rc}")
         return out, lse
+
+    # -- 8-bit inputs ----------------------------------------------------------
+    def attention_fp8(self, q8, k8, v8, descale_q, descale_k, descale_v, causal=False,
+                      window=(-1, -1), scale=None):
+        """Attention of 8-bit e4m3 inputs (uint8 codes, layouts as attention())
+        whose real values are descale * decode(code): the values are decoded
+        exactly (decode_e4m3) and scaled in fp64 (exact: a 4-bit significand
+        times an fp32 factor), then the plain definition applies."""
+        q = decode_e4m3(q8) * float(descale_q)
+        k = decode_e4m3(k8) * float(descale_k)
+        v = decode_e4m3(v8) * float(descale_v)
+        d = q.shape[-1]
+        return self.attention(q, k, v, causal=causal, window=window,
+                              scale=_scale(scale, d))
 
     # -- gradients (padded batch) -------------------------------------------
     def attention_bwd(self, q, k, v, dout, causal=False, window=(-1, -1), scale=None):
@@ -298,6 +331,10 @@ def attention_decode(*a, **kw):
 
 def attention_decode_paged(*a, **kw):
     return default().attention_decode_paged(*a, **kw)
+
+
+def attention_fp8(*a, **kw):
+    return default().attention_fp8(*a, **kw)
 
 
 def attention_bwd(*a, **kw):

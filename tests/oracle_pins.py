@@ -735,6 +735,43 @@ def pin_softcap_saturates(orc):
     assert np.abs(o0 - o1).max() < 1e-10 and np.abs(l0 - l1).max() < 1e-10
 
 
+def pin_e4m3_decoder(orc):
+    """Every one of the 256 e4m3 codes decodes to torch's float8_e4m3fn value
+    (a library routine of the same format), NaN exactly at the two NaN codes;
+    spot values from the format: 0x38 = 1, 0x7e = 448 (the largest), 0x08 =
+    2^-6 (the smallest normal), 0x01 = 2^-9 (the smallest subnormal)."""
+    import oracle as _o
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = _o.decode_e4m3(codes.numpy())
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and int(nan.sum()) == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert got[0x38] == 1.0 and got[0x7E] == 448.0 and got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9
+    assert got[0xB8] == -1.0 and got[0x80] == 0.0
+
+
+def pin_fp8_attention(orc):
+    """The 8-bit entry of the oracle is the plain definition on descaled
+    values: equal to attention() on torch-decoded inputs times the scales;
+    all-zero query codes give LSE = ln(#visible)."""
+    rng = _rng(80)
+    B, Sq, Sk, Hq, Hkv, d = 1, 6, 9, 4, 2, 8
+    mk = lambda *sh: torch.from_numpy(rng.integers(0, 256, size=sh).astype(np.uint8))
+    q8, k8, v8 = mk(B, Sq, Hq, d), mk(B, Sk, Hkv, d), mk(B, Sk, Hkv, d)
+    for t in (q8, k8, v8):                     # no NaN codes
+        t[(t & 0x7F) == 0x7F] = 0x38
+    dq, dk, dv = 0.01, 0.02, 0.5
+    dec = lambda t, s: t.view(torch.float8_e4m3fn).to(torch.float64).numpy() * s
+    for causal in (False, True):
+        o1, l1 = orc.attention_fp8(q8, k8, v8, dq, dk, dv, causal=causal, scale=0.3)
+        o2, l2 = orc.attention(dec(q8, dq), dec(k8, dk), dec(v8, dv), causal=causal, scale=0.3)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    _, lz = orc.attention_fp8(torch.zeros_like(q8), k8, v8, dq, dk, dv, causal=True)
+    for i in range(Sq):
+        assert abs(lz[0, 0, i] - math.log(i + Sk - Sq + 1)) < 1e-13
+
+
 PINS = [
     pin_worked_example, pin_torch_sdpa, pin_zero_query_closed_form, pin_varlen_zero_query,
     pin_decode_zero_query, pin_constant_v, pin_single_visible_key, pin_one_hot_values,
@@ -744,5 +781,5 @@ PINS = [
     pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_identities,
     pin_bwd_gqa_equals_repeated_mha, pin_paged_equals_contiguous, pin_paged_append,
     pin_paged_append_zero_query, pin_mod_torch_reference, pin_mod_neutral,
-    pin_alibi_zero_query_closed_form, pin_softcap_saturates,
+    pin_alibi_zero_query_closed_form, pin_softcap_saturates, pin_e4m3_decoder, pin_fp8_attention,
 ]
