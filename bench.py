@@ -8,7 +8,8 @@ U{1024..32768}, split 1024 + combine) is timed beside it and reported under
 "decode"; the same keys in a shuffled pool of 256-row pages, with each
 sequence's last key appended by the call (fa_decode_paged: append, split,
 combine), under "decode_paged"; the prefill with ALiBi and/or soft-capping
-(fa_fwd_mod) under "forward_modifiers"; and the backward (fa_bwd, three kernels) of
+(fa_fwd_mod) under "forward_modifiers"; the prefill on 8-bit e4m3 inputs
+(fa_fwd_fp8) under "forward_fp8"; and the backward (fa_bwd, three kernels) of
 the prefill workload under "backward".  Inputs are seeded synthetic tensors already resident in
 HBM.
 
@@ -133,6 +134,34 @@ def bench_fwd_mod(steps, warmup, w, qd, kd, vd, softcap, alibi):
     return {"workload": f"{w.name}_{name}", "value": round(tf, 2), "unit": "TFLOP/s",
             "ms_per_step": round(wall, 4), "event_ms_per_call": round(ev, 4),
             "frac_bf16_mfma_peak": round(tf / metrics.PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_fp8(steps, warmup, w):
+    """fa_fwd_fp8 on the prefill workload's shape: fp32 N(0, 1) inputs drawn
+    from its seed, quantised per tensor to e4m3 (synth.gen_fp8), resident in
+    HBM; two kernels per call (V transpose into the workspace, attention).
+    FLOP as the 16-bit forward; peaks: fp8 dense MFMA and bf16 for context."""
+    (q8, k8, v8), (dq, dk, dv) = synth.gen_fp8(w.seed, w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.sigma)
+    dev = "cuda:0"
+    q8, k8, v8 = q8.to(dev), k8.to(dev), v8.to(dev)
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.Hq, w.Sq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.fwd_fp8_workspace_bytes(w.B, w.Hkv, w.Sk, w.d), dtype=torch.uint8, device=dev)
+    work = metrics.fwd_work(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.causal, w.window)
+
+    def step():
+        fa.fwd_fp8(q8, k8, v8, dq, dk, dv, causal=w.causal, window=w.window, out=out, lse=lse,
+                   workspace=ws)
+
+    wall, ev = _timed(step, steps, warmup)
+    tf = work["flop"] / (ev * 1e-3) / 1e12
+    res = {"workload": f"{w.name}_fp8_e4m3", "value": round(tf, 2), "unit": "TFLOP/s",
+           "ms_per_step": round(wall, 4), "event_ms_per_call": round(ev, 4),
+           "frac_fp8_mfma_peak": round(tf / metrics.PEAK_FP8_TFLOPS, 4),
+           "frac_bf16_mfma_peak": round(tf / metrics.PEAK_BF16_TFLOPS, 4), "kernels_per_call": 2}
+    del q8, k8, v8, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_decode(steps, warmup):
@@ -265,6 +294,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-mods", action="store_true", help="skip the score-modifier legs")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit forward leg")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle time for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -312,6 +342,8 @@ def main():
     }
     if mods is not None:
         line["forward_modifiers"] = mods
+    if not args.no_fp8:
+        line["forward_fp8"] = bench_fp8(max(10, args.steps // 2), max(3, args.warmup // 2), w)
     if not args.no_decode:
         del q
         line["decode"] = bench_decode(max(10, args.steps // 2), max(3, args.warmup // 2))

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa355.so")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
 # MFMA results of the forward kernel are consumed by VALU code (the softmax):
 # keep them in arch VGPRs instead of accumulation registers.  Its arithmetic
 # never makes a NaN from finite inputs, so NaNs need not be honoured: v_max

@@ -306,6 +306,54 @@ fa_status_t fa_decode_paged(const void* q, void* k_pages, void* v_pages,
     return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
 }
 
+size_t fa_fwd_fp8_workspace_bytes(int B, int Hkv, int Sk, int d) {
+    if (B < 1 || Hkv < 1 || Sk < 1 || d < 1) return 0;
+    return (size_t)B * Hkv * d * (((size_t)Sk + 63) / 64 * 64);
+}
+
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse, int B,
+                       int Hq, int Hkv, int Sq, int Sk, int d, int causal, int window_left,
+                       int window_right, float softmax_scale, float descale_q, float descale_k,
+                       float descale_v, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    // dtype BF16 here only selects the checks; q/k/v are 8-bit, out is bf16
+    fa_status_t st = check_common(q, k, v, out, lse, B, Hq, Hkv, d, window_left, window_right,
+                                  softmax_scale, FA_BF16, Sk == 0);
+    if (st != FA_OK) return st;
+    if (!std::isfinite(descale_q) || !std::isfinite(descale_k) || !std::isfinite(descale_v) ||
+        descale_q <= 0.f || descale_k <= 0.f || descale_v <= 0.f)
+        return fail(FA_ERR_INVALID_ARG, "descale factors must be finite and > 0");
+    if (Sq < 0 || Sk < 0) return fail(FA_ERR_INVALID_ARG, "Sq, Sk must be >= 0 (got %d, %d)", Sq, Sk);
+    if (Sq == 0) return ok();
+    if ((st = check_seq_bytes(Sq, Hq, d, "q/out")) != FA_OK) return st;
+    if ((st = check_seq_bytes(Sk, Hkv, d, "k/v")) != FA_OK) return st;
+    const size_t need = fa_fwd_fp8_workspace_bytes(B, Hkv, Sk, d);
+    if (need > 0 && (!workspace || !aligned16(workspace)))
+        return fail(FA_ERR_WORKSPACE, "workspace must be non-null and 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    fa::Fp8Params p{};
+    p.q = q; p.k = k; p.v = v; p.vt = workspace; p.o = out; p.lse = lse;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sq = Sq; p.Sk = Sk; p.sk_pad = (Sk + 63) / 64 * 64;
+    p.gw = fa::fwd_heads_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.nqt = (Sq + p.bm - 1) / p.bm;
+    p.q_tok_stride = (long long)Hq * d;
+    p.kv_tok_stride = (long long)Hkv * d;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    // scores are scaled in fp32: c = |scale| dq dk log2(e), kept >= FLT_MIN
+    // (masked scores are -inf); a negative scale flips the sign bit of q
+    p.c = std::fmax(std::fabs(softmax_scale) * descale_q * descale_k * fa::kLog2e_host,
+                    1.17549435e-38f);
+    p.qsign = softmax_scale < 0.f ? 0x80808080u : 0u;
+    p.descale_v = descale_v;
+    p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
+    if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    return launch_status(fa::launch_fwd_fp8(p, d, stream));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq) {
     if (B < 1 || Hq < 1 || Sq < 1) return 0;
     return (size_t)B * Hq * Sq * sizeof(float);

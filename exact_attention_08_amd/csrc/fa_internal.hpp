@@ -36,6 +36,27 @@ struct FwdParams {
     float sc_c;                 // soft-capping: cap * log2(e)
 };
 
+// Forward on 8-bit (e4m3) Q, K, V (padded batch).  Strides in bytes.
+struct Fp8Params {
+    const void* q;              // [B, Sq, Hq, d] e4m3
+    const void* k;              // [B, Sk, Hkv, d] e4m3
+    const void* v;              // [B, Sk, Hkv, d] e4m3
+    void* vt;                   // workspace: V^T [B, Hkv, d, sk_pad], 64-key blocks permuted
+    void* o;                    // [B, Sq, Hq, d] bf16
+    float* lse;                 // [B, Hq, Sq] or null
+    int B, Hq, Hkv, G;
+    int Sq, Sk, sk_pad;         // sk_pad = Sk rounded up to 64
+    int nqt;
+    long long q_tok_stride;     // Hq * d
+    long long kv_tok_stride;    // Hkv * d
+    int causal, wl, wr;
+    float c;                    // |scale| * descale_q * descale_k * log2(e)
+    uint32_t qsign;             // 0x80808080 when scale < 0 (q negated exactly), else 0
+    float descale_v;
+    int xcd_groups, gw, bm;
+};
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s);
+
 // Decode split kernel + combine kernel.
 struct DecodeParams {
     const void* q;

@@ -23,7 +23,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_E
           4: "FA_ERR_HIP"}
 
 # Every symbol include/fa.h declares.
-EXPORTS = ("fa_fwd", "fa_fwd_mod", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
+EXPORTS = ("fa_fwd", "fa_fwd_mod", "fa_fwd_fp8_workspace_bytes", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
            "fa_decode_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
            "fa_last_error")
 
@@ -55,6 +55,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_fwd.restype = I
         lib.fa_fwd_mod.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P, F, I, P]
         lib.fa_fwd_mod.restype = I
+        lib.fa_fwd_fp8_workspace_bytes.argtypes = [I, I, I, I]
+        lib.fa_fwd_fp8_workspace_bytes.restype = ctypes.c_size_t
+        lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, F, F, F, P,
+                                   ctypes.c_size_t, P]
+        lib.fa_fwd_fp8.restype = I
         lib.fa_fwd_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P]
         lib.fa_fwd_varlen.restype = I
         lib.fa_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -148,6 +153,36 @@ def fwd_mod(q, k, v, *, causal=False, window=(-1, -1), softmax_scale=None, alibi
                           int(bool(causal)), int(window[0]), int(window[1]),
                           _scale(softmax_scale, d), _ptr(alibi_slopes), float(softcap),
                           _DTYPE[q.dtype], _stream()))
+    return out, lse
+
+
+def fwd_fp8_workspace_bytes(B: int, Hkv: int, Sk: int, d: int) -> int:
+    return int(load().fa_fwd_fp8_workspace_bytes(B, Hkv, Sk, d))
+
+
+def fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, *, causal=False, window=(-1, -1),
+            softmax_scale=None, out=None, lse=None, workspace=None):
+    """8-bit forward: q8 [B,Sq,Hq,d], k8/v8 [B,Sk,Hkv,d] uint8 e4m3 codes on the GPU with
+    per-tensor descales -> (out [B,Sq,Hq,d] bf16, lse [B,Hq,Sq] fp32)."""
+    for t in (q8, k8, v8):
+        _require(t.is_cuda and t.dtype == torch.uint8 and t.is_contiguous() and t.dim() == 4,
+                 "q8, k8, v8 must be contiguous 4-d uint8 GPU tensors (e4m3 codes)")
+    _require(k8.shape == v8.shape, "k8 and v8 must have one shape")
+    B, Sq, Hq, d = q8.shape
+    _, Sk, Hkv, _ = k8.shape
+    lib = load()
+    need = int(lib.fa_fwd_fp8_workspace_bytes(B, Hkv, Sk, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q8.device)
+    if out is None:
+        out = torch.empty((B, Sq, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    _check(lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk,
+                          d, int(bool(causal)), int(window[0]), int(window[1]),
+                          _scale(softmax_scale, d), float(descale_q), float(descale_k),
+                          float(descale_v), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream()))
     return out, lse
 
 

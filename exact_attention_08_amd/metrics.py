@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import numpy as np
 
+PEAK_FP8_TFLOPS = 5033.2       # dense fp8 MFMA, 256 CU x 2.4 GHz x 8192 FLOP/clk
 PEAK_BF16_TFLOPS = 2516.6      # dense bf16/fp16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0          # HBM3E
 

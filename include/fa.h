@@ -108,6 +108,31 @@ fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, f
                        const float* alibi_slopes, float softcap,
                        fa_dtype_t dtype, hipStream_t stream);
 
+/* Bytes of workspace fa_fwd_fp8 needs: V transposed per K/V head,
+ * B * Hkv * d * (Sk rounded up to 64) bytes. */
+size_t fa_fwd_fp8_workspace_bytes(int B, int Hkv, int Sk, int d);
+
+/* Padded batch on 8-bit inputs (the "FlashAttention" explainer page: the
+ * later versions use lower-precision number formats, "What it is"; the
+ * project summary lists FP8; no recipe is given).  q, k, v hold e4m3 codes
+ * (the OCP 8-bit float: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; 448 the largest value) whose real values are descale_{q,k,v} times
+ * the code values (one fp32 factor per tensor, > 0).  Both products run on
+ * 8-bit matrix instructions with fp32 accumulation; the softmax weights are
+ * rounded to e4m3 for P.V; statistics are fp32.  out is bf16.
+ *   q : [B, Sq, Hq, d] e4m3    k, v : [B, Sk, Hkv, d] e4m3
+ *   out : [B, Sq, Hq, d] bf16  lse : [B, Hq, Sq] fp32 (may be NULL)
+ *   workspace : DEVICE scratch of at least fa_fwd_fp8_workspace_bytes(B,
+ *               Hkv, Sk, d) bytes (V transposed by a first kernel), owned
+ *               by the caller, contents ignored; may be NULL when Sk == 0
+ * Other arguments, masks, LSE and errors as fa_fwd.  Two kernels are
+ * enqueued (V transpose, attention). */
+fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                       int causal, int window_left, int window_right, float softmax_scale,
+                       float descale_q, float descale_k, float descale_v,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Packed sequences (flash_attn_varlen_func; "The One-Line Change ..." page,
  * sequence packing).  B sequences; sequence z owns query rows
  * [cu_seqlens_q[z], cu_seqlens_q[z+1]) and key rows

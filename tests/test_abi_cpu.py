@@ -28,11 +28,12 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_api():
-    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_mod", "fa_fwd_varlen",
+    assert declared_functions() == sorted(["fa_fwd", "fa_fwd_mod", "fa_fwd_fp8_workspace_bytes",
+                                           "fa_fwd_fp8", "fa_fwd_varlen",
                                            "fa_decode_workspace_bytes",
                                            "fa_decode_kvcache", "fa_decode_paged",
                                            "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
@@ -105,6 +106,34 @@ def test_fwd_mod_rejects(lib, kw, status):
 
 def test_fwd_mod_empty_query_is_a_noop(lib):
     assert fwd_mod(lib, alibi=FAKE, softcap=3.0, Sq=0) == 0
+
+
+def fp8(lib, ws=FAKE, ws_bytes=1 << 30, dq=0.01, dk=0.01, dv=0.01, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, Sq=8, Sk=8, d=128,
+             causal=1, wl=-1, wr=-1, scale=0.125)
+    a.update(kw)
+    return lib.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Sq"], a["Sk"], a["d"], a["causal"], a["wl"], a["wr"], a["scale"], dq,
+                          dk, dv, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=MISALIGNED), 1), (dict(dq=0.0), 1), (dict(dk=-1.0), 1),
+    (dict(dv=math.nan), 1), (dict(dq=math.inf), 1), (dict(d=96), 2), (dict(Hq=6, Hkv=4), 1),
+    (dict(ws=None), 3), (dict(ws=FAKE + 8), 3), (dict(ws_bytes=1 * 2 * 128 * 64 - 1), 3),
+    (dict(scale=math.nan), 1), (dict(wl=-3), 1),
+])
+def test_fp8_rejects(lib, kw, status):
+    assert fp8(lib, **kw) == status
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_fp8_workspace_bytes(lib):
+    f = lib.fa_fwd_fp8_workspace_bytes
+    assert f(4, 8, 4096, 128) == 4 * 8 * 128 * 4096
+    assert f(1, 2, 65, 64) == 2 * 64 * 128
+    assert f(1, 2, 0, 64) == 0
+    assert fp8(lib, Sq=0) == 0
 
 
 def varlen(lib, cu_q=FAKE, cu_k=FAKE, B=2, maxq=8, maxk=8, total_q=10, d=128, **kw):
