@@ -40,6 +40,11 @@ namespace fa {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+template <int V>
+struct fp8_int_c {
+    static constexpr int value = V;
+};
+
 template <int D>
 struct Fp8Geo {
     static constexpr int HR = 32;                 // rows per half
@@ -231,17 +236,26 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
         return ring + ((jt - tile_lo) % T::STAGES) * T::TILE;
     };
     // tiles outside [tile_lo, tile_last] get zero records (zeros, no memory access)
-    auto issue = [&](int jt) __attribute__((always_inline)) {
+    struct SetCopy {
+        i32x4 krs, vrs;
+        uint32_t dst;
+    };
+    auto set_copy = [&](int jt) __attribute__((always_inline)) {
         const bool valid = jt >= tile_lo && jt <= tile_last;
         const int rows = valid ? min(sk - jt * T::BN, T::BN) : 0;
         const i32x4 krs = make_rsrc(kseq + (long long)jt * T::BN * tok_kv, rows * tok_kv);
         // V^T rows are sk_pad long; a tile is 64 bytes of each of D rows
         const i32x4 vrs = make_rsrc(vtrow + (long long)jt * T::BN,
                                     valid ? (D - 1) * p.sk_pad + T::BN : 0);
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot(jt)));
+        return SetCopy{krs, vrs, (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(slot(jt)))};
+    };
+    auto copy_one = [&](const SetCopy& sc, int i) __attribute__((always_inline)) {
+        dma16_to_lds(scalar_rsrc(dma_isk[i] ? sc.krs : sc.vrs), sc.dst + dma_loff[i], dma_voff[i], 0);
+    };
+    auto issue = [&](int jt) __attribute__((always_inline)) {
+        const SetCopy sc = set_copy(jt);
 #pragma unroll
-        for (int i = 0; i < T::LPS; ++i)
-            dma16_to_lds(scalar_rsrc(dma_isk[i] ? krs : vrs), dst + dma_loff[i], dma_voff[i], 0);
+        for (int i = 0; i < T::LPS; ++i) copy_one(sc, i);
     };
     // At the top of step jt this wave's copies of tiles jt and jt + 1 have
     // landed (those of jt + 2 .. jt + STAGES - 3 may fly); the barrier then
@@ -365,6 +379,79 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
         stile[hs] = jt;
     };
 
+    // The same region with one matrix instruction per slot and, beside each,
+    // an equal share of the other half's exponentials with their packing
+    // and sums (a slot never waits for its own results); hook(i) adds the
+    // slot's operand loads or copies.  sched_barrier(0) keeps the order:
+    // with one wave per SIMD the matrix and vector pipes only overlap as
+    // far as the instruction stream alternates them.
+    auto fast_region = [&](auto hsc, int jt, bool masked_other, auto&& hook)
+        __attribute__((always_inline)) {
+        constexpr int hs = decltype(hsc)::value, hp = 1 - hs;
+        constexpr int NS = 2 * T::KC + T::DB;         // matrix slots
+        constexpr int EPS = 32 / NS;                  // weights per slot
+        static_assert(EPS * NS == 32 && EPS % 4 == 0, "whole packed words per slot");
+        if (masked_other) apply_mask(hp);
+        const bool first = m_run[hp] == -INFINITY;
+        const float m_use = first ? 0.f : m_run[hp];
+        float part[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (i < 2 * T::KC) {
+                const int st = i / T::KC, kc = i % T::KC;
+                sacc[hs][st] = mfma_f8(kbuf[st][kc], qop[hs][kc], kc == 0 ? f32x16{} : sacc[hs][st]);
+            } else {
+                const int db = i - 2 * T::KC;
+                oacc[hs][db] = mfma_f8(vbuf[db], pb[hs], oacc[hs][db]);
+            }
+            hook(i);
+            float x[EPS];
+#pragma unroll
+            for (int j = 0; j < EPS; ++j) {
+                const int el = i * EPS + j;
+                x[j] = exp2_fast(fmaf(sacc[hp][el >> 4][el & 15], c, -m_use));
+            }
+#pragma unroll
+            for (int w = 0; w < EPS / 4; ++w)
+                pb[hp][i * (EPS / 4) + w] = (int)pack4_fp8(x[4 * w], x[4 * w + 1], x[4 * w + 2], x[4 * w + 3]);
+            float t2[EPS / 2];
+#pragma unroll
+            for (int j = 0; j < EPS / 2; ++j) t2[j] = x[2 * j] + x[2 * j + 1];
+#pragma unroll
+            for (int wdt = EPS / 4; wdt >= 1; wdt >>= 1)
+#pragma unroll
+                for (int j = 0; j < wdt; ++j) t2[j] += t2[j + wdt];
+            part[i] = t2[0];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int wdt = NS / 2; wdt >= 1; wdt >>= 1)
+#pragma unroll
+            for (int j = 0; j < wdt; ++j) part[j] += part[j + wdt];
+        float sum = part[0];
+        if ((__builtin_amdgcn_ballot_w64(first) | __builtin_amdgcn_ballot_w64(sum > 256.f)) != 0ull) {
+            asm volatile("");
+            float mx = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[hp][st][e]);
+            mx = max_halves(mx);
+            const float mnew = fmaxf(m_run[hp], mx * c);
+            const bool raise = mnew > m_run[hp] + kFp8RescaleThreshold;
+            const float alpha = raise ? exp2_fast(m_run[hp] - mnew) : 1.f;
+            l_run[hp] *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[hp][db][e] *= alpha;
+            m_run[hp] = raise ? mnew : m_run[hp];
+            sum = exps(hp, m_run[hp] == -INFINITY ? 0.f : m_run[hp]);
+        }
+        l_run[hp] += sum;
+        stile[hs] = jt;
+    };
+
     // first step: no previous tile (P = 0, V = 0), no S of half B yet
 #pragma unroll
     for (int st = 0; st < 2; ++st)
@@ -413,26 +500,29 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
         }
         // step jt: S(jt) and P.V of jt - 1; the step after the last tile
         // only finishes the previous one
-        for (int jt = tile_lo; jt <= tile_last + 1; ++jt) {
+        for (int jt = tile_lo; jt <= tile_last; ++jt) {
             if (jt > tile_lo) sync_step();
-            issue(jt + T::STAGES - 2);
-            const bool last = jt > tile_last;
             // the other half's newest S: half B of jt - 1 (region 0), half A
             // of jt (region 1)
             const bool mB = !interior(1, jt - 1), mA = !interior(0, jt);
-            region(0, jt, mB, !last, true);
-            region(1, jt, mA, !last, !last);
-            if (last) break;
-            // operands of the next step: K of jt + 1, V^T of jt
+            // region 0 spreads this step's copies over its slots; region 1
+            // reloads each operand register right after its last use: K of
+            // jt + 1 and V^T of jt for the next step
+            const SetCopy sc = set_copy(jt + T::STAGES - 2);
+            fast_region(fp8_int_c<0>{}, jt, mB, [&](int i) __attribute__((always_inline)) {
+                if (i < T::LPS) copy_one(sc, i);
+            });
             const uint8_t* tn = slot(jt + 1);
             const uint8_t* tc = slot(jt);
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int kc = 0; kc < T::KC; ++kc) kbuf[st][kc] = acc_regs8(k_op(tn, st, kc));
-#pragma unroll
-            for (int db = 0; db < T::DB; ++db) vbuf[db] = acc_regs8(v_op(tc, db));
+            fast_region(fp8_int_c<1>{}, jt, mA, [&](int i) __attribute__((always_inline)) {
+                if (i < 2 * T::KC) kbuf[i / T::KC][i % T::KC] = acc_regs8(k_op(tn, i / T::KC, i % T::KC));
+                else vbuf[i - 2 * T::KC] = acc_regs8(v_op(tc, i - 2 * T::KC));
+            });
         }
+        // the step after the last tile: P.V of the last tile only (its
+        // operands are in registers; no LDS access, no copies)
+        region(0, tile_last + 1, !interior(1, tile_last), false, true);
+        region(1, tile_last + 1, false, false, false);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
