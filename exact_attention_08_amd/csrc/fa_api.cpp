@@ -401,10 +401,10 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out,
     p.c2 = softmax_scale * fa::kLog2e_host;
     p.nkb = (Sk + fa::kBwdKeysPerWg - 1) / fa::kBwdKeysPerWg;
     p.gw = fa::fwd_heads_per_wg(p.G);
-    const int bmq = 32 * fa::kBwdWaves / p.gw;
+    const int bmq = 32 * fa::bwd_dq_waves(d) / p.gw;
     p.nqb = (Sq + bmq - 1) / bmq;
     if ((long long)p.nkb * Hkv * B * fa::kBwdThreads > kMaxGridThreads ||
-        (long long)p.nqb * (Hq / p.gw) * B * fa::kBwdThreads > kMaxGridThreads ||
+        (long long)p.nqb * (Hq / p.gw) * B * 64 * fa::bwd_dq_waves(d) > kMaxGridThreads ||
         (long long)B * Sq * Hq * (d / 8) > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
     return launch_status(fa::launch_bwd(p, d, dtype == FA_BF16, stream));

@@ -43,10 +43,10 @@
 
 namespace fa {
 
-template <int D>
+template <int D, int WAVES = kBwdWaves>
 struct BwdGeo {
     static constexpr int R = 32;                 // rows (or keys) per tile and per wave
-    static constexpr int NW = kBwdWaves;         // waves per work-group
+    static constexpr int NW = WAVES;             // waves per work-group
     static constexpr int KS = D / 16;            // reduction steps over d
     static constexpr int DB = D / 32;            // 32-column blocks of d
     static constexpr int TE = R * D;             // elements per tile
@@ -369,11 +369,14 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // dQ of one query block: gw query heads of one K/V head (wave w: head
-// hg*gw + w%gw) and 128/gw rows (wave w: rows q0 + 32*(w/gw) .. +31).
+// hg*gw + w%gw) and 32*NW/gw rows (wave w: rows q0 + 32*(w/gw) .. +31).
+// NW = 8 at d = 128: two waves per SIMD, so one wave's vector work (the
+// weights, dS) runs beside the other's matrix instructions, and each K/V
+// stage copied to LDS serves twice the rows.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * bwd_dq_waves(D)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdParams p) {
-    using T = BwdGeo<D>;
+    using T = BwdGeo<D, bwd_dq_waves(D)>;
     constexpr int TE = T::TE;
     // stage s: K (A order), V (A order), K (T order)
     constexpr int NS = kDqStages;
@@ -548,7 +551,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
     }
     if (p.Sq > 0) {
         const long long n = (long long)p.nqb * (p.Hq / p.gw) * p.B;
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16>), dim3((unsigned)n), dim3(kBwdThreads), 0, s, p);
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16>), dim3((unsigned)n), dim3(64 * bwd_dq_waves(D)), 0, s, p);
     }
     return hipGetLastError();
 }

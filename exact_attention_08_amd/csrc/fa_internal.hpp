@@ -128,6 +128,9 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr float kLog2e_host = 1.4426950408889634f;
 constexpr int kBwdWaves = 4;       // waves per backward work-group
 constexpr int kBwdThreads = 64 * kBwdWaves;
+// dQ work-group: 32 rows per wave, two waves per SIMD; 8 waves split the
+// three 8 KB tiles of a d = 128 stage evenly, 4 those of d = 64
+constexpr int bwd_dq_waves(int d) { return d == 128 ? 8 : 4; }
 constexpr int kBwdKeysPerWg = 32 * kBwdWaves;   // dK/dV work-group: 32 keys per wave
 
 }  // namespace fa
