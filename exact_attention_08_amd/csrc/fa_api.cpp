@@ -403,7 +403,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out,
     p.gw = fa::fwd_heads_per_wg(p.G);
     const int bmq = 32 * fa::bwd_dq_waves(d) / p.gw;
     p.nqb = (Sq + bmq - 1) / bmq;
-    if ((long long)p.nkb * Hkv * B * fa::kBwdThreads > kMaxGridThreads ||
+    if ((long long)p.nkb * Hkv * B * 64 * fa::kBwdDkdvWaves > kMaxGridThreads ||
         (long long)p.nqb * (Hq / p.gw) * B * 64 * fa::bwd_dq_waves(d) > kMaxGridThreads ||
         (long long)B * Sq * Hq * (d / 8) > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");

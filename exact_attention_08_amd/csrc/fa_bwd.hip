@@ -13,7 +13,7 @@
 //
 //   fa_bwd_dot_kernel   D_i = dO_i . O_i for every row (O = the forward's
 //                       output), the row term of dS below;
-//   fa_bwd_dkdv_kernel  one work-group per 128 keys of one K/V head: for
+//   fa_bwd_dkdv_kernel  one work-group per 256 keys of one K/V head: for
 //                       every query head of the group and every 32-row query
 //                       block that sees those keys
 //                           S = Q K^T,  P = exp2(S c2 - LSE_2),  dP = dO V^T,
@@ -34,10 +34,11 @@
 //     operand (d x 16 rows) of a 32x32x16 MFMA is two contiguous 512 B reads.
 // A ring of stages holds the tiles (4 in the dK/dV kernel, whose stage also
 // carries the rows' LSE and D, 5 in the dQ kernel); one barrier per step
-// publishes a stage and frees the oldest one for the next copy.  The operands that stay fixed
-// for a work-group (K and V of the wave's keys in the dK/dV kernel, Q and dO
-// of the wave's rows in the dQ kernel) are loaded once into the accumulation
-// registers, which MFMAs read directly.
+// publishes a stage and frees the oldest one for the next copy.  The
+// operands that stay fixed for a work-group (K and V of the wave's keys in
+// the dK/dV kernel, Q and dO of the wave's rows in the dQ kernel) are loaded
+// once into registers (in the dQ kernel the accumulation registers, which
+// MFMAs read directly).  Both kernels run two waves per SIMD at d = 128.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -166,12 +167,18 @@ __global__ __launch_bounds__(256) void fa_bwd_dot_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV of 128 keys of one K/V head.  Wave w owns keys k0 + 32w .. +31;
-// the work-group walks (query head of the group) x (32-row query block).
+// dK and dV of 32*NW keys of one K/V head.  Wave w owns keys k0 + 32w ..
+// +31; the work-group walks (query head of the group) x (32-row query
+// block).  NW = 8: two waves per SIMD (one's vector work runs beside the
+// other's matrix instructions) and each Q/dO stage copied to LDS serves 256
+// keys.  At two waves per SIMD a wave has 256 registers; using none of the
+// accumulation registers keeps all 256 as ordinary ones (the compiler
+// splits the budget in halves once any accumulation register is used), and
+// the rows' LSE and D are read from the stage where they are used.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kBwdDkdvWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
-    using T = BwdGeo<D>;
+    using T = BwdGeo<D, kBwdDkdvWaves>;
     constexpr int TE = T::TE;
     // stage s: Q (A order), dO (A order), Q (T order), dO (T order), then
     // the LSE and D of the block's rows (256 bytes each, the first 128 used)
@@ -194,6 +201,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const int sq = p.Sq, sk = p.Sk, delta = sk - sq;
     const int k0 = kb * kBwdKeysPerWg;
     const int k1 = min(k0 + kBwdKeysPerWg, sk) - 1;
+    static_assert(kBwdKeysPerWg == T::R * T::NW, "keys per work-group");
     const int kw0 = k0 + T::R * wave;           // this wave's first key
     const int j = kw0 + (lane & 31);            // this lane's key
 
@@ -223,8 +231,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) {
             const int off = j * tok_kv + (16 * ks + 8 * g) * 2;
-            kop[ks] = to_acc_regs(__builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0));
-            vop[ks] = to_acc_regs(__builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0));
+            kop[ks] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+            vop[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
         }
     }
 
@@ -292,45 +300,41 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const float* d_s = lse_s + 64;
 
             // LSE (log2 units) and D of rows i0 + acc_row(e) + 4g
-            float lse2[16], dd[16];
-            {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * q4 + 4 * g);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 8 * q4 + 4 * g);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        // a row with no visible key has LSE = -inf: its
-                        // weights are 0 (exp2(x - inf)), never inf
-                        lse2[4 * q4 + r] = l4[r] == -INFINITY ? INFINITY : l4[r] * kLog2e;
-                        dd[4 * q4 + r] = d4[r];
-                    }
-                }
-            }
-
             f32x16 sacc = {}, dpacc = {};
 #pragma unroll
             for (int ks = 0; ks < T::KS; ++ks) {
                 sacc = mfma32x32x16<BF16>(a_operand<D>(qa, ks, lane), kop[ks], sacc);
                 dpacc = mfma32x32x16<BF16>(a_operand<D>(oa, ks, lane), vop[ks], dpacc);
             }
-            // P and dS; element e is row i0 + acc_row(e) + 4g of key j
+            // P and dS; element e is row i0 + acc_row(e) + 4g of key j.  The
+            // rows' LSE (log2 units) and D are read from the stage four at a
+            // time, where they are used.
             const int tb = j - delta - i0 - 4 * g;
             const int e_lo = tb - t_hi, e_hi = tb - t_lo;   // visible iff e_lo <= acc_row(e) <= e_hi
             u32x4 pp[2], pds[2];
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                float pv[2], dv2[2];
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * q4 + 4 * g);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 8 * q4 + 4 * g);
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int ce = acc_row(e + u);
-                    const bool vis = ce >= e_lo && ce <= e_hi && j < sk;
-                    const float x = exp2_fast(fmaf(sacc[e + u], p.c2, -lse2[e + u]));
-                    pv[u] = vis ? x : 0.f;
-                    dv2[u] = pv[u] * (dpacc[e + u] - dd[e + u]);
+                for (int e2 = 0; e2 < 4; e2 += 2) {
+                    const int e = 4 * q4 + e2;
+                    float pv[2], dv2[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int ce = acc_row(e + u);
+                        const bool vis = ce >= e_lo && ce <= e_hi && j < sk;
+                        // a row with no visible key has LSE = -inf: its
+                        // weights are 0 (exp2(x - inf)), never inf
+                        const float l = l4[e2 + u];
+                        const float lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+                        const float x = exp2_fast(fmaf(sacc[e + u], p.c2, -lse2));
+                        pv[u] = vis ? x : 0.f;
+                        dv2[u] = pv[u] * (dpacc[e + u] - d4[e2 + u]);
+                    }
+                    pp[e >> 3][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
+                    pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
                 }
-                pp[e >> 3][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
-                pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
             }
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -547,7 +551,7 @@ static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
     }
     if (p.Sk > 0) {
         const long long n = (long long)p.nkb * p.Hkv * p.B;
-        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)n), dim3(kBwdThreads), 0, s, p);
+        hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)n), dim3(64 * kBwdDkdvWaves), 0, s, p);
     }
     if (p.Sq > 0) {
         const long long n = (long long)p.nqb * (p.Hq / p.gw) * p.B;

@@ -131,6 +131,7 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 // dQ work-group: 32 rows per wave, two waves per SIMD; 8 waves split the
 // three 8 KB tiles of a d = 128 stage evenly, 4 those of d = 64
 constexpr int bwd_dq_waves(int d) { return d == 128 ? 8 : 4; }
-constexpr int kBwdKeysPerWg = 32 * kBwdWaves;   // dK/dV work-group: 32 keys per wave
+constexpr int kBwdDkdvWaves = 8;   // dK/dV work-group: 32 keys per wave, two waves per SIMD
+constexpr int kBwdKeysPerWg = 32 * kBwdDkdvWaves;
 
 }  // namespace fa
