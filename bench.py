@@ -9,7 +9,7 @@ U{1024..32768}, split 1024 + combine) is timed beside it and reported under
 sequence's last key appended by the call (fa_decode_paged: append, split,
 combine), under "decode_paged"; the prefill with ALiBi and/or soft-capping
 (fa_fwd_mod) under "forward_modifiers"; the prefill on 8-bit e4m3 inputs
-(fa_fwd_fp8) under "forward_fp8"; and the backward (fa_bwd, three kernels) of
+(fa_fwd_fp8) under "forward_fp8"; and the backward (fa_bwd, two kernels) of
 the prefill workload under "backward".  Inputs are seeded synthetic tensors already resident in
 HBM.
 
@@ -230,7 +230,7 @@ def bench_decode_paged(steps, warmup, page_size=256):
 
 
 def bench_backward(steps, warmup, w):
-    """fa_bwd (three kernels) on the same workload, with the GPU forward's own
+    """fa_bwd (two kernels) on the same workload, with the GPU forward's own
     O and LSE and a seeded incoming gradient, all resident in HBM."""
     q, k, v = synth.generate(w)
     dev = "cuda:0"
@@ -251,7 +251,7 @@ def bench_backward(steps, warmup, w):
     res = {"workload": w.name, "value": round(tf, 2), "unit": "TFLOP/s",
            "ms_per_step": round(wall, 4), "event_ms_per_call": round(ev, 4),
            "frac_bf16_mfma_peak": round(tf / metrics.PEAK_BF16_TFLOPS, 4),
-           "algorithmic_flop": work["flop"], "kernels_per_call": 3,
+           "algorithmic_flop": work["flop"], "kernels_per_call": 2,
            "flop_convention": "10*d per visible pair per query head (2.5x forward)"}
     del qd, kd, vd, god, o, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()

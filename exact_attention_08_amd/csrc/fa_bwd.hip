@@ -11,15 +11,16 @@
 // stays on chip in a kernel of its own, so no partial sums go to memory and
 // no floating-point atomics are used (results are bitwise reproducible):
 //
-//   fa_bwd_dot_kernel   D_i = dO_i . O_i for every row (O = the forward's
-//                       output), the row term of dS below;
 //   fa_bwd_dkdv_kernel  one work-group per 256 keys of one K/V head: for
 //                       every query head of the group and every 32-row query
 //                       block that sees those keys
 //                           S = Q K^T,  P = exp2(S c2 - LSE_2),  dP = dO V^T,
 //                           dS = P (dP - D),  dV^T += dO^T P,  dK^T += Q^T dS;
-//   fa_bwd_dq_kernel    one work-group per query block (the query heads of
-//                       one K/V head): for every 32-key tile it sees
+//   fa_bwd_dq_kernel    (enqueued first) one work-group per query block (the
+//                       query heads of one K/V head); first the row term of dS,
+//                       D_i = dO_i . O_i (O = the forward's output), which
+//                       it also stores for the next kernel; then for every
+//                       32-key tile it sees
 //                           S^T = K Q^T,  dP^T = V dO^T,  the same P and dS,
 //                           dQ^T += K^T dS^T;
 // with c2 = scale * log2(e), LSE_2 = LSE * log2(e), and dK, dQ multiplied by
@@ -129,43 +130,6 @@ __device__ __forceinline__ u32x4 t_operand(const uint16_t* tile, int kk, int db,
 __device__ __forceinline__ constexpr int acc_row(int e) { return 8 * (e >> 2) + (e & 3); }
 
 // ---------------------------------------------------------------------------
-// D_i = dO_i . O_i, one row of d elements per D/8 lanes (16 bytes each).
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void fa_bwd_dot_kernel(BwdParams p) {
-    constexpr int LPR = D / 8;                  // lanes per row
-    const long long nrows = (long long)p.B * p.Sq * p.Hq;
-    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long row = gid / LPR;            // ((b * Sq + i) * Hq + h)
-    const int part = (int)(gid % LPR);
-    float acc = 0.f;
-    if (row < nrows) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>((const uint16_t*)p.dout + row * D + part * 8);
-        const u32x4 o = *reinterpret_cast<const u32x4*>((const uint16_t*)p.o + row * D + part * 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // exact widening of both 16-bit halves, fp32 products and sums
-            const uint32_t x = a[w], y = o[w];
-            float xl, xh, yl, yh;
-            if constexpr (BF16) {
-                xl = __builtin_bit_cast(float, x << 16); xh = __builtin_bit_cast(float, x & 0xffff0000u);
-                yl = __builtin_bit_cast(float, y << 16); yh = __builtin_bit_cast(float, y & 0xffff0000u);
-            } else {
-                const f16x2 xv = __builtin_bit_cast(f16x2, x), yv = __builtin_bit_cast(f16x2, y);
-                xl = (float)xv[0]; xh = (float)xv[1]; yl = (float)yv[0]; yh = (float)yv[1];
-            }
-            acc = fmaf(xl, yl, acc);
-            acc = fmaf(xh, yh, acc);
-        }
-    }
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < nrows && part == 0) {
-        const long long h = row % p.Hq, bi = row / p.Hq;   // bi = b * Sq + i
-        const long long b = bi / p.Sq, i = bi - b * p.Sq;
-        p.dsum[(b * p.Hq + h) * p.Sq + i] = acc;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // dK and dV of 32*NW keys of one K/V head.  Wave w owns keys k0 + 32w ..
 // +31; the work-group walks (query head of the group) x (32-row query
@@ -423,25 +387,50 @@ void fa_bwd_dq_kernel(BwdParams p) {
 
     // ---- Q and dO of this wave's rows as B operands (lane: row l%32) ------
     u32x4 qop[T::KS], oop[T::KS];
+    float dd_row;
     {
         const long long base = ((long long)b * sq * p.Hq + hq) * D * 2;
         const auto qrs = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.q + base), (short)0,
                                                            sq * tok_q, 0x00020000);
         const auto ors = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.dout + base), (short)0,
                                                            sq * tok_q, 0x00020000);
+        const auto outrs = __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)p.o + base), (short)0,
+                                                             sq * tok_q, 0x00020000);
+        // the row term D = dO . O of this lane's row: each lane holds half of
+        // the row's d values (fp32 products and sums of exactly widened
+        // 16-bit values), the lane l ^ 32 the other half
+        float dpart = 0.f;
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks) {
             const int off = row * tok_q + (16 * ks + 8 * g) * 2;
+            const u32x4 go = __builtin_amdgcn_raw_buffer_load_b128(ors, off, 0, 0);
+            const u32x4 oo = __builtin_amdgcn_raw_buffer_load_b128(outrs, off, 0, 0);
             qop[ks] = to_acc_regs(__builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0));
-            oop[ks] = to_acc_regs(__builtin_amdgcn_raw_buffer_load_b128(ors, off, 0, 0));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t x = go[w], y = oo[w];
+                float xl, xh, yl, yh;
+                if constexpr (BF16) {
+                    xl = __builtin_bit_cast(float, x << 16); xh = __builtin_bit_cast(float, x & 0xffff0000u);
+                    yl = __builtin_bit_cast(float, y << 16); yh = __builtin_bit_cast(float, y & 0xffff0000u);
+                } else {
+                    const f16x2 xv = __builtin_bit_cast(f16x2, x), yv = __builtin_bit_cast(f16x2, y);
+                    xl = (float)xv[0]; xh = (float)xv[1]; yl = (float)yv[0]; yh = (float)yv[1];
+                }
+                dpart = fmaf(xl, yl, dpart);
+                dpart = fmaf(xh, yh, dpart);
+            }
+            oop[ks] = to_acc_regs(go);
         }
+        dd_row = sum_halves(dpart);
     }
     float lse2 = INFINITY, dd = 0.f;                      // rows past the end: no weight
     if (row < sq) {
         const long long ri = ((long long)b * p.Hq + hq) * sq + row;
         const float l = p.lse[ri];
         lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-        dd = p.dsum[ri];
+        dd = dd_row;
+        if (g == 0) p.dsum[ri] = dd;                      // for the dK/dV kernel, which runs next
     }
     // this lane's visible key interval, relative to its first key offset 4g
     int rel_lo, rel_hi;
@@ -543,19 +532,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
 
 template <int D, bool BF16>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-    const long long nrows = (long long)p.B * p.Sq * p.Hq;
-    if (nrows > 0) {
-        const long long threads = nrows * (D / 8);
-        hipLaunchKernelGGL((fa_bwd_dot_kernel<D, BF16>), dim3((unsigned)((threads + 255) / 256)),
-                           dim3(256), 0, s, p);
+    // dQ first: it also writes the row terms D the dK/dV kernel reads
+    if (p.Sq > 0) {
+        const long long n = (long long)p.nqb * (p.Hq / p.gw) * p.B;
+        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16>), dim3((unsigned)n), dim3(64 * bwd_dq_waves(D)), 0, s, p);
     }
     if (p.Sk > 0) {
         const long long n = (long long)p.nkb * p.Hkv * p.B;
         hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, BF16>), dim3((unsigned)n), dim3(64 * kBwdDkdvWaves), 0, s, p);
-    }
-    if (p.Sq > 0) {
-        const long long n = (long long)p.nqb * (p.Hq / p.gw) * p.B;
-        hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16>), dim3((unsigned)n), dim3(64 * bwd_dq_waves(D)), 0, s, p);
     }
     return hipGetLastError();
 }

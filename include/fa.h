@@ -242,8 +242,9 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq);
  *   other arguments as for fa_fwd.  Sq == 0 sets dk and dv to zero; Sk == 0
  *   sets dq to zero (k, v, dk, dv may then be NULL).  Keys no row sees get
  *   dk = dv = 0; rows with no visible key get dq = 0.
- * Three kernels are enqueued on `stream`; none accumulates with atomics, so
- * repeated calls give bitwise identical results. */
+ * Two kernels are enqueued on `stream` (dQ with the row terms D, then dK
+ * and dV); none accumulates with atomics, so repeated calls give bitwise
+ * identical results. */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    int B, int Hq, int Hkv, int Sq, int Sk, int d,
