@@ -36,6 +36,8 @@ BWD_CASES = [
     ("large_group", 1, 16, 1, 130, 130, 128, "bf16", True, (-1, -1), None, 213),
     ("sigma_large_scores", 1, 4, 2, 256, 256, 128, "bf16", True, (-1, -1), 0.5, 214),
     ("long_causal", 1, 4, 1, 1000, 1000, 128, "bf16", True, (-1, -1), None, 215),
+    ("group3_window_left", 1, 6, 2, 260, 260, 128, "bf16", True, (64, -1), None, 216),
+    ("group6_d64_fp16", 1, 6, 1, 300, 333, 64, "fp16", False, (-1, -1), None, 217),
 ]
 
 

@@ -34,6 +34,10 @@ FP8_CASES = [
     ("long_causal", 1, 4, 1, 1000, 1000, 128, True, (-1, -1), None, 1.0, 708),
     ("window_two_sided_d64", 1, 2, 1, 300, 300, 64, False, (50, 30), None, 1.0, 709),
     ("single_key", 1, 2, 2, 50, 1, 128, False, (-1, -1), None, 1.0, 710),
+    ("group3", 1, 6, 2, 200, 200, 128, True, (-1, -1), None, 1.0, 712),
+    ("group16", 1, 16, 1, 130, 130, 128, True, (-1, -1), None, 1.0, 713),
+    ("d64_causal_gqa", 2, 8, 2, 300, 300, 64, True, (-1, -1), None, 1.0, 714),
+    ("window_left_long", 1, 4, 4, 700, 700, 128, True, (200, -1), None, 0.5, 715),
 ]
 
 

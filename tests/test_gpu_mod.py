@@ -37,6 +37,10 @@ MOD_CASES = [
      1.0, 607),
     ("both_d64_fp16_long", 1, 4, 2, 1000, 1000, 64, "fp16", True, (-1, -1), None, 50.0, True, 0.5,
      608),
+    ("alibi_group3_d64_fp16", 1, 6, 2, 300, 300, 64, "fp16", True, (-1, -1), None, 0.0, True, 1.0,
+     611),
+    ("softcap5_group16", 1, 16, 1, 130, 130, 128, "bf16", True, (-1, -1), 0.3, 5.0, False, 1.0, 612),
+    ("alibi_sq_gt_sk", 1, 4, 2, 300, 77, 128, "bf16", True, (-1, -1), None, 0.0, True, 1.0, 613),
 ]
 
 
