@@ -32,8 +32,9 @@
 // w_c = exp(LSE_c - M): LSE = M + ln(sum w_c), O = sum w_c O_c / sum w_c,
 // summed in split order (deterministic), several partial rows in flight.
 //
-// Paged cache (the project summary's "paged KV cache support"; the
-// explainer's advice to use paged cache layouts): the keys of sequence b
+// Paged cache (the project summary lists paged KV cache support for the
+// cached-decode call; the explainer advises paged cache layouts): the keys
+// of sequence b
 // live in pages of page_size token rows, token t at row t % page_size of
 // page block_table[b][t / page_size].  page_size is a multiple of 32, so
 // each 32-key block of the split kernel lies in one page and costs one
