@@ -34,9 +34,8 @@
 //
 // Paged cache (the project summary lists paged KV cache support for the
 // cached-decode call; the explainer advises paged cache layouts): the keys
-// of sequence b
-// live in pages of page_size token rows, token t at row t % page_size of
-// page block_table[b][t / page_size].  page_size is a multiple of 32, so
+// of sequence b live in pages of page_size token rows, token t at row
+// t % page_size of page block_table[b][t / page_size].  page_size is a multiple of 32, so
 // each 32-key block of the split kernel lies in one page and costs one
 // table read; the buffer resource of a block then starts at that page row.
 // With an append, a small kernel first writes the new token's key and value
