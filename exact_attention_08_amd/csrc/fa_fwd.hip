@@ -480,12 +480,7 @@ void fa_fwd_kernel(FwdParams p) {
     };
     // invisible scores of half h's tile jt -> -inf
     auto apply_mask = [&](int h, int jt) __attribute__((always_inline)) {
-        const int lo = rel_lo[h] - jt * T::BN, hi = rel_hi[h] - jt * T::BN;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int off = 8 * (e >> 2) + (e & 3);
-            sacc[h][e] = (off >= lo && off <= hi) ? sacc[h][e] : -INFINITY;
-        }
+        mask_acc32(sacc[h], rel_lo[h] - jt * T::BN, rel_hi[h] - jt * T::BN);
     };
     auto qk = [&](int h, const u32x4 (&kq)[T::KS]) __attribute__((always_inline)) {
 #pragma unroll

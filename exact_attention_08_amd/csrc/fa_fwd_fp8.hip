@@ -300,11 +300,7 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
         const int base = stile[h] * T::BN;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int key = base + 32 * st + 8 * (e >> 2) + (e & 3);
-                sacc[h][st][e] = (key >= rel_lo[h] && key <= rel_hi[h]) ? sacc[h][st][e] : -INFINITY;
-            }
+            mask_acc32(sacc[h][st], rel_lo[h] - base - 32 * st, rel_hi[h] - base - 32 * st);
     };
     // exps of half h with max m: packs P and returns this lane's fp32 sum
     auto exps = [&](int h, float m_use) __attribute__((always_inline)) {
