@@ -278,7 +278,7 @@ void fa_decode_split_kernel(DecodeParams p) {
                 const uint32_t pk = pack2<BF16>(x0, x1);
                 pb[2 * h + (e >> 1)] = pk;
                 l_run += x0 + x1;
-                lr_run = dot2_ones<BF16>(pk, lr_run);
+                lr_run = sum2_16<BF16>(pk, lr_run);
             }
 
         // O^T += V^T P^T ; accumulator db row m is column m*DB + db

@@ -71,16 +71,22 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, uint32_t hi_src
     return __builtin_amdgcn_perm(hi_src, lo_src, SEL_HI ? 0x07060302u : 0x05040100u);
 }
 
-// acc + lo + hi of a dword holding two 16-bit values (v_dot2 against (1, 1)).
+// (acc + lo) + hi of a dword holding two 16-bit values, on the plain VALU:
+// a bf16 value is the high half of its fp32 value, so a mask and a shift
+// give both exactly; fp16 values are converted.  (v_dot2 against (1, 1)
+// would be one instruction, but it issues through the matrix pipe and
+// waits behind the MFMAs it should overlap.)
 template <bool BF16>
-__device__ __forceinline__ float dot2_ones(uint32_t packed, float acc) {
+__device__ __forceinline__ float sum2_16(uint32_t packed, float acc) {
+    float lo, hi;
     if constexpr (BF16) {
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
-                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+        lo = __builtin_bit_cast(float, packed << 16);
+        hi = __builtin_bit_cast(float, packed & 0xffff0000u);
     } else {
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed),
-                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
+        lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed & 0xffffu));
+        hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed >> 16));
     }
+    return (acc + lo) + hi;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -62,8 +62,7 @@
 // exponentiated with the stale max first; only when a lane's sum of weights
 // exceeds 2^8 (or a row has no max yet) is the true tile max taken and the
 // tile redone, so unmasked steps compute no row max at all.  O is normalised
-// by the sum of the 16-bit probabilities fed to P.V (v_dot2 against (1, 1)),
-// LSE by the fp32 sum.
+// by the sum of the 16-bit probabilities fed to P.V, LSE by the fp32 sum.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -432,7 +431,7 @@ void fa_fwd_kernel(FwdParams p) {
         for (int e = 0; e < 16; e += 2) {
             const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
             pb[h][e >> 3][(e & 7) >> 1] = pk;
-            r2[(e >> 1) & 1] = dot2_ones<BF16>(pk, r2[(e >> 1) & 1]);
+            r2[(e >> 1) & 1] = sum2_16<BF16>(pk, r2[(e >> 1) & 1]);
         }
 #pragma unroll
         for (int w = 8; w >= 1; w >>= 1)
@@ -540,7 +539,7 @@ void fa_fwd_kernel(FwdParams p) {
                     a[j] = x[2 * j] + x[2 * j + 1];
                 }
                 if ((2 * j + 1) / EPS + 2 == i) {
-                    r2[j & 1] = dot2_ones<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
+                    r2[j & 1] = sum2_16<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
                     pin(r2[j & 1]);
                     if (j & 1) bsum[j >> 1] = a[j - 1] + a[j];
                 }
@@ -556,7 +555,7 @@ void fa_fwd_kernel(FwdParams p) {
                 a[j] = x[2 * j] + x[2 * j + 1];
             }
             if ((2 * j + 1) / EPS + 2 >= NS) {
-                r2[j & 1] = dot2_ones<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
+                r2[j & 1] = sum2_16<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
                 if (j & 1) bsum[j >> 1] = a[j - 1] + a[j];
             }
         }
