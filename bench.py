@@ -41,9 +41,13 @@ COPY_BYTES = 1 << 30          # plain-copy calibration: 1 GiB read + 1 GiB writt
 
 
 def source_hash(name: str) -> str:
-    """sha256 of a kernel source file (ties profiled counters to the code)."""
-    with open(os.path.join(KERNEL_SRC, name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 of a kernel source file and the two headers every kernel file
+    includes (ties profiled counters to the code)."""
+    h = hashlib.sha256()
+    for f in (name, "fa_device.hpp", "fa_internal.hpp"):
+        with open(os.path.join(KERNEL_SRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def profiled_traffic(summary: str, src: str):
@@ -73,9 +77,24 @@ def copy_calibration():
                       "copies": 3}), flush=True)
 
 
+# Untimed calls before each leg's W warm-up calls, so that the timed steps
+# run at the GPU's sustained clock: from idle the clocks ramp up over the
+# first tens of milliseconds of load (measured: the forward's first 20
+# launches average 0.74 ms, the next ones 0.54-0.55 ms; after 1 s idle the
+# first 20 average 0.65 ms again).  Legs are separated by host work (input
+# generation), so every leg settles anew.
+CLOCK_SETTLE_S = 0.25
+
+
 def _timed(fn, steps: int, warmup: int):
-    """W untimed calls, then exactly K timed calls bracketed by synchronize;
-    returns (wall ms per step, event ms per step on the launch stream)."""
+    """Clock settling (CLOCK_SETTLE_S of untimed calls), W untimed calls,
+    then exactly K timed calls bracketed by synchronize; returns (wall ms per
+    step, event ms per step on the launch stream)."""
+    t_end = time.perf_counter() + CLOCK_SETTLE_S
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -324,6 +343,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_s": CLOCK_SETTLE_S,
         "ms_per_step": round(wall, 5),
         "higher_is_better": True,
         "scaling": "weak",
