@@ -28,9 +28,10 @@
 //     row; 16-bit halves are regrouped in registers.
 // Each split writes a normalised fp32 partial O_c and its LSE_c.
 //
-// Combine kernel: one wave per (sequence, query head); with M = max_c LSE_c,
-// w_c = exp(LSE_c - M): LSE = M + ln(sum w_c), O = sum w_c O_c / sum w_c,
-// summed in split order (deterministic), several partial rows in flight.
+// Combine kernel: D/64 waves per (sequence, query head), 64 columns each;
+// with M = max_c LSE_c, w_c = exp(LSE_c - M): LSE = M + ln(sum w_c),
+// O = sum w_c O_c / sum w_c, summed in split order (deterministic), several
+// partial rows in flight.
 //
 // Paged cache (the project summary lists paged KV cache support for the
 // cached-decode call; the explainer advises paged cache layouts): the keys
@@ -384,27 +385,29 @@ void fa_decode_split_kernel(DecodeParams p) {
     }
 }
 
+// Lane l of wave part owns column 64 part + l.  (Two waves per 128-column
+// row rather than one: the kernel is latency bound, and twice the waves in
+// flight take ~2 us off its ~9 us.)
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) {
-    constexpr int PER = D / 64;        // columns per lane
+    constexpr int CW = D / 64;         // waves per row
     constexpr int UNROLL = 32;         // partial rows in flight per lane
-    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w = wv / CW, part = wv % CW;
     const int lane = threadIdx.x & 63;
     if (w >= p.B * p.Hq) return;
     const int b = w / p.Hq, hq = w - b * p.Hq;
     const int L = decode_len(p, b);
     const int n = (L + p.split - 1) / p.split;
     const long long row0 = ((long long)b * p.Hq + hq) * p.nsplit;
-    const float* src = p.ws_o + row0 * D + lane * PER;
+    const float* src = p.ws_o + row0 * D + part * 64 + lane;
 
     // The first 64 LSEs (lane s: split s) and the first UNROLL partial rows
     // are requested together: the rows do not depend on the weights.
     float lse0 = lane < n ? p.ws_lse[row0 + lane] : -INFINITY;
-    float x0[UNROLL][PER];
+    float x0[UNROLL];
 #pragma unroll
-    for (int k = 0; k < UNROLL; ++k)
-#pragma unroll
-        for (int u = 0; u < PER; ++u) x0[k][u] = k < n ? src[(long long)k * D + u] : 0.f;
+    for (int k = 0; k < UNROLL; ++k) x0[k] = k < n ? src[(long long)k * D] : 0.f;
 
     // M = max_c LSE_c, lanes over splits
     float M = lse0;
@@ -413,20 +416,16 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
 
-    float acc[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) acc[u] = 0.f;
-    float sum = 0.f;
+    float acc = 0.f, sum = 0.f;
     if (M != -INFINITY) {
         // lane s holds the weight of split s0 + s; the sums below run in
         // split order (deterministic)
         auto weight = [&](float ls) { return ls == -INFINITY ? 0.f : exp2_fast((ls - M) * kLog2e); };
-        auto add_row = [&](float wl, int k, const float* x) __attribute__((always_inline)) {
+        auto add_row = [&](float wl, int k, float x) __attribute__((always_inline)) {
             const float wk = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
             sum += wk;
-#pragma unroll
-            for (int u = 0; u < PER; ++u) acc[u] = fmaf(wk, x[u], acc[u]);
+            acc = fmaf(wk, x, acc);
         };
         float wl = weight(lse0);
 #pragma unroll
@@ -436,12 +435,10 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
             if (s0 > 0) wl = s0 + lane < n ? weight(p.ws_lse[row0 + s0 + lane]) : 0.f;
             const int m = min(64, n - s0);
             for (int c0 = s0 == 0 ? UNROLL : 0; c0 < m; c0 += UNROLL) {
-                float x[UNROLL][PER];
+                float x[UNROLL];
 #pragma unroll
                 for (int k = 0; k < UNROLL; ++k)
-#pragma unroll
-                    for (int u = 0; u < PER; ++u)
-                        x[k][u] = c0 + k < m ? src[(long long)(s0 + c0 + k) * D + u] : 0.f;
+                    x[k] = c0 + k < m ? src[(long long)(s0 + c0 + k) * D] : 0.f;
 #pragma unroll
                 for (int k = 0; k < UNROLL; ++k)
                     if (c0 + k < m) add_row(wl, c0 + k, x[k]);
@@ -449,14 +446,9 @@ __global__ __launch_bounds__(256) void fa_decode_combine_kernel(DecodeParams p) 
         }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    uint16_t* orow = (uint16_t*)p.o + ((long long)b * p.Hq + hq) * D + lane * PER;
-    if constexpr (PER == 2) {
-        *reinterpret_cast<uint32_t*>(orow) = pack2<BF16>(acc[0] * inv, acc[1] * inv);
-    } else {
-        const uint32_t pk = pack2<BF16>(acc[0] * inv, 0.f);
-        orow[0] = (uint16_t)(pk & 0xffffu);
-    }
-    if (p.lse != nullptr && lane == 0)
+    uint16_t* orow = (uint16_t*)p.o + ((long long)b * p.Hq + hq) * D + part * 64 + lane;
+    *orow = (uint16_t)(pack2<BF16>(acc * inv, 0.f) & 0xffffu);
+    if (p.lse != nullptr && lane == 0 && part == 0)
         p.lse[(long long)b * p.Hq + hq] = sum > 0.f ? M + log2_fast(sum) * kLn2 : -INFINITY;
 }
 
@@ -476,7 +468,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
                            dim3(kDecodeThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const long long ncomb = ((long long)p.B * p.Hq + 3) / 4;
+    const long long ncomb = ((long long)p.B * p.Hq * (D / 64) + 3) / 4;
     hipLaunchKernelGGL((fa_decode_combine_kernel<D, BF16>), dim3((unsigned)ncomb), dim3(256), 0, s,
                        p);
     return hipGetLastError();
