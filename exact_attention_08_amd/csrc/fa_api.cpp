@@ -356,7 +356,7 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, f
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq) {
     if (B < 1 || Hq < 1 || Sq < 1) return 0;
-    return (size_t)B * Hq * Sq * sizeof(float);
+    return 2 * (size_t)B * Hq * Sq * sizeof(float);
 }
 
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
@@ -392,6 +392,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out,
     p.q = q; p.k = k; p.v = v; p.o = out; p.dout = dout; p.lse = lse;
     p.dq = dq; p.dk = dk; p.dv = dv;
     p.dsum = static_cast<float*>(workspace);
+    p.lse2 = p.dsum + (size_t)B * Hq * Sq;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk;
     p.q_tok_stride = (long long)Hq * d;

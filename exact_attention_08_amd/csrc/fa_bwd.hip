@@ -221,7 +221,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         const i32x4 ors = uniform_rsrc(make_rsrc((const char*)p.dout + off, rows * tok_q));
         const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + (s % NS) * SE));
         const long long rb = ((long long)b * p.Hq + h) * sq + i0;
-        dma4_to_lds(uniform_rsrc(make_rsrc(p.lse + rb, rows * 4)), dst + 4 * TE * 2, lane * 4);
+        dma4_to_lds(uniform_rsrc(make_rsrc(p.lse2 + rb, rows * 4)), dst + 4 * TE * 2, lane * 4);
         dma4_to_lds(uniform_rsrc(make_rsrc(p.dsum + rb, rows * 4)), dst + 4 * TE * 2 + 256, lane * 4);
 #pragma unroll
         for (int c = 0; c < LPS - 2; ++c) {
@@ -275,6 +275,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             // time, where they are used.
             const int tb = j - delta - i0 - 4 * g;
             const int e_lo = tb - t_hi, e_hi = tb - t_lo;   // visible iff e_lo <= acc_row(e) <= e_hi
+            const uint32_t vis = j < sk ? vis_bits(e_lo, e_hi) : 0u;
             u32x4 pp[2], pds[2];
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -286,14 +287,11 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                     float pv[2], dv2[2];
 #pragma unroll
                     for (int u = 0; u < 2; ++u) {
-                        const int ce = acc_row(e + u);
-                        const bool vis = ce >= e_lo && ce <= e_hi && j < sk;
-                        // a row with no visible key has LSE = -inf: its
-                        // weights are 0 (exp2(x - inf)), never inf
-                        const float l = l4[e2 + u];
-                        const float lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-                        const float x = exp2_fast(fmaf(sacc[e + u], p.c2, -lse2));
-                        pv[u] = vis ? x : 0.f;
+                        // LSE in log2 units, +inf for a row with no
+                        // visible key (weights exp2(x - inf) = 0, never inf)
+                        const float x = exp2_fast(fmaf(sacc[e + u], p.c2, -l4[e2 + u]));
+                        pv[u] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) &
+                                                              bit_mask(vis, acc_row(e + u)));
                         dv2[u] = pv[u] * (dpacc[e + u] - d4[e2 + u]);
                     }
                     pp[e >> 3][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
@@ -430,7 +428,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
         const float l = p.lse[ri];
         lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
         dd = dd_row;
-        if (g == 0) p.dsum[ri] = dd;                      // for the dK/dV kernel, which runs next
+        if (g == 0) {                                     // for the dK/dV kernel, which runs next
+            p.dsum[ri] = dd;
+            p.lse2[ri] = lse2;
+        }
     }
     // this lane's visible key interval, relative to its first key offset 4g
     int rel_lo, rel_hi;
@@ -492,16 +493,16 @@ void fa_bwd_dq_kernel(BwdParams p) {
                 sacc = mfma32x32x16<BF16>(a_operand<D>(ka, ks, lane), qop[ks], sacc);
                 dpacc = mfma32x32x16<BF16>(a_operand<D>(va, ks, lane), oop[ks], dpacc);
             }
-            const int lo = rel_lo - jt * T::R, hi = rel_hi - jt * T::R;
+            const uint32_t vis = vis_bits(rel_lo - jt * T::R, rel_hi - jt * T::R);
             u32x4 pds[2];
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
                 float dv2[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int off = acc_row(e + u);
                     const float x = exp2_fast(fmaf(sacc[e + u], p.c2, -lse2));
-                    const float pv = (off >= lo && off <= hi) ? x : 0.f;
+                    const float pv = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) &
+                                                                   bit_mask(vis, acc_row(e + u)));
                     dv2[u] = pv * (dpacc[e + u] - dd);
                 }
                 pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);

@@ -127,14 +127,21 @@ __device__ __forceinline__ float sum_halves(float x) {
 // offsets outside [lo, hi] become -inf.  Bit k of vis marks offset k
 // visible; each element takes its bit, sign-extended to a whole-word mask
 // (one bit-field extract and one bitwise select, no compares).
-__device__ __forceinline__ void mask_acc32(f32x16& s, int lo, int hi) {
+__device__ __forceinline__ uint32_t vis_bits(int lo, int hi) {
     lo = min(max(lo, 0), 31);
     hi = min(max(hi, -1), 30);
-    const uint32_t vis = __builtin_amdgcn_ubfe(0xffffffffu, 0, max(hi + 1 - lo, 0)) << lo;
+    return __builtin_amdgcn_ubfe(0xffffffffu, 0, max(hi + 1 - lo, 0)) << lo;
+}
+// all ones when bit off of vis is set, else zero
+__device__ __forceinline__ uint32_t bit_mask(uint32_t vis, int off) {
+    return (uint32_t)((int)(vis << (31 - off)) >> 31);
+}
+__device__ __forceinline__ void mask_acc32(f32x16& s, int lo, int hi) {
+    const uint32_t vis = vis_bits(lo, hi);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int off = 8 * (e >> 2) + (e & 3);
-        const uint32_t m = (uint32_t)((int)(vis << (31 - off)) >> 31);
+        const uint32_t m = bit_mask(vis, off);
         const float x = s[e];   // (a bit_cast of the vector element itself reads element 0)
         s[e] = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & m) | (0xff800000u & ~m));
     }

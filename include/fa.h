@@ -223,8 +223,9 @@ fa_status_t fa_decode_paged(const void* q, void* k_pages, void* v_pages,
                             void* workspace, size_t workspace_bytes,
                             fa_dtype_t dtype, hipStream_t stream);
 
-/* Bytes of fp32 workspace fa_bwd needs: one value per query row and head
- * (D_i = dO_i . O_i). */
+/* Bytes of fp32 workspace fa_bwd needs: two values per query row and head
+ * (D_i = dO_i . O_i, and LSE_i in log2 units), written by the first kernel
+ * for the second. */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq);
 
 /* Gradients of the padded-batch attention (the training backward): given

@@ -228,7 +228,7 @@ def test_bwd_rejects(lib, kw, status):
 
 
 def test_bwd_workspace_bytes(lib):
-    assert lib.fa_bwd_workspace_bytes(4, 32, 4096) == 4 * 32 * 4096 * 4
+    assert lib.fa_bwd_workspace_bytes(4, 32, 4096) == 2 * 4 * 32 * 4096 * 4
     assert lib.fa_bwd_workspace_bytes(0, 32, 4096) == 0
 
 
