@@ -125,7 +125,11 @@ __device__ __forceinline__ u32x4 in_acc_regs(u32x4 v) {
 //     u = cap log2(e) tanh(scale s / cap) - slope log2(e) |pos_i - j|
 // (each part only when enabled); tanh(y) = 1 - 2 / (exp2(2 y log2 e) + 1).
 // MOD = 0 compiles to the unmodified kernel.
-template <int D, bool BF16, bool VARLEN, int MOD>
+// BAND (sliding windows, where most steps of a wave need masks): every
+// computed step runs in the interleaved two-region pipeline, the masks
+// applied out of line at the start of a region; otherwise masked steps
+// take a generic order and only unmasked ones the pipeline.
+template <int D, bool BF16, bool VARLEN, int MOD, bool BAND>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fa_fwd_kernel(FwdParams p) {
     using T = FwdGeo<D>;
@@ -234,6 +238,10 @@ void fa_fwd_kernel(FwdParams p) {
     const int act_hi = max(pw_hi[0], pw_hi[1]) + 1;
     const int fast_lo = max(in_lo[0], in_lo[1]);
     const int fast_hi = min(in_hi[0], in_hi[1]);
+    // (band form: over the halves that compute anything)
+    const bool he0 = pw_lo[0] <= pw_hi[0], he1 = pw_lo[1] <= pw_hi[1];
+    const int band_lo = he0 ? (he1 ? min(pw_lo[0], pw_lo[1]) : pw_lo[0]) : (he1 ? pw_lo[1] : 1);
+    const int band_hi = he0 ? (he1 ? max(pw_hi[0], pw_hi[1]) : pw_hi[0]) + 1 : (he1 ? pw_hi[1] + 1 : 0);
 
     // ---- K/V ring in LDS, filled by DMA -----------------------------------
     // Set s = (K_s, V_s); 2*TILE_BLOCKS 1 KB blocks, wave w issues blocks w,
@@ -372,9 +380,9 @@ void fa_fwd_kernel(FwdParams p) {
         const int kk = q / T::DB, db = q % T::DB;
         return ds_read_tr16(vt + ((2 * kk + hh) * T::DB + db) * 256 + lane * 4);
     };
-    auto load_k_now = [&](const uint16_t* kt) __attribute__((always_inline)) {
+    auto load_k_now = [&](auto pc, const uint16_t* kt) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) kbuf[0][ks] = in_acc_regs(k_load(kt, ks));
+        for (int ks = 0; ks < T::KS; ++ks) kbuf[decltype(pc)::value][ks] = in_acc_regs(k_load(kt, ks));
     };
     auto load_v_now = [&](const uint16_t* vt) __attribute__((always_inline)) {
 #pragma unroll
@@ -504,9 +512,13 @@ void fa_fwd_kernel(FwdParams p) {
     // the same region.  sched_barrier(0) fences keep the order: with one
     // wave per SIMD the matrix and vector pipes only overlap as far as the
     // instruction stream alternates them.
-    auto fast_region = [&](auto hsc, int jt, const u32x4 (&kq)[T::KS],
+    auto fast_region = [&](auto hsc, int jt, bool mask, const u32x4 (&kq)[T::KS],
                            const u32x4 (&vq)[T::KK][T::DB], auto&& load) __attribute__((always_inline)) {
         constexpr int hs = decltype(hsc)::value, hp = 1 - hs;
+        if (__builtin_expect(mask, 0)) {      // band form only: S of half hp, tile jt - 1 + hs
+            asm volatile("");                  // a real branch, out of line
+            apply_mask(hp, jt - 1 + hs);
+        }
         constexpr int NS = T::KS + T::KK * T::DB;       // MFMA slots
         constexpr int EPS = 16 / NS;                    // exponentials per slot
         static_assert(EPS * NS == 16, "whole exponentials per slot");
@@ -566,8 +578,11 @@ void fa_fwd_kernel(FwdParams p) {
     // is in kbuf[P] and V_{jt-1} in vbuf[1-P]; the step loads K_{jt+1} and
     // V_jt into the other two buffers (the loads are issued one per slot and
     // claimed at the end of the step, so no slot waits for LDS).
-    auto fast_step = [&](auto pc, int jt, bool even) __attribute__((always_inline)) {
+    // With M (band form) the step masks whatever it exponentiates that
+    // needs it: S_B(jt-1) in the first region, S_A(jt) in the second.
+    auto fast_step = [&](auto pc, auto mc, int jt, bool even) __attribute__((always_inline)) {
         constexpr int P = decltype(pc)::value;
+        constexpr bool M = decltype(mc)::value;
         // this step's set copies go out one every few slots: issued all at
         // once by the four waves of a CU they queue at its address unit
         const SetCopy sc = set_copy(jt + T::STAGES - 2);
@@ -577,12 +592,12 @@ void fa_fwd_kernel(FwdParams p) {
         constexpr int NQ = T::KK * T::DB;
         u32x4 kn[T::KS];
         u32x2 vlo[NQ], vhi[NQ];
-        fast_region(int_c<0>{}, jt, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
+        fast_region(int_c<0>{}, jt, M && !interior(1, jt - 1), kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
             if (i < T::KS) kn[i] = k_load(kt, i);
             else vlo[i - T::KS] = v_half(vt, i - T::KS, 0);
             if (i % CSTEP == CSTEP / 2) copy_one(sc, i / CSTEP);
         });
-        fast_region(int_c<1>{}, jt, kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
+        fast_region(int_c<1>{}, jt, M && !interior(0, jt), kbuf[P], vbuf[1 - P], [&](int i) __attribute__((always_inline)) {
             if (i < NQ) vhi[i] = v_half(vt, i, 1);
         });
 #pragma unroll
@@ -600,7 +615,7 @@ void fa_fwd_kernel(FwdParams p) {
     auto step_masked = [&](int jt, bool even) __attribute__((always_inline)) {
         issue(jt + T::STAGES - 2);
         if (jt >= act_lo && jt <= act_hi) {
-            load_k_now(kslot(jt));
+            load_k_now(int_c<0>{}, kslot(jt));
             qk(0, kbuf[0]);
             softmax_tile(1);
             js[0] = jt;
@@ -665,8 +680,44 @@ void fa_fwd_kernel(FwdParams p) {
     for (int kk = 0; kk < T::KK; ++kk)
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) vbuf[1][kk][db] = (u32x4){0u, 0u, 0u, 0u};
+    if constexpr (BAND) {           // the first computed step may have parity 1
+#pragma unroll
+        for (int kk = 0; kk < T::KK; ++kk)
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db) vbuf[0][kk][db] = (u32x4){0u, 0u, 0u, 0u};
+    }
 
-    if (ntiles > 0) {
+    if (ntiles > 0 && BAND) {
+        for (int s = tile_lo; s < tile_lo + T::STAGES - 2; ++s) issue(s);
+        sync_pair();
+        // steps r = 0 .. ntiles; this wave computes [ra, rb], each step with
+        // the static parity of r; outside it only copies and barriers
+        const int ra = max(band_lo - tile_lo, 0), rb = min(band_hi - tile_lo, ntiles);
+        auto copy_step = [&](int r) __attribute__((always_inline)) {
+            issue(tile_lo + r + T::STAGES - 2);
+            if (r & 1) sync_pair();
+        };
+        int r = 0;
+        for (; r < ra; ++r) copy_step(r);
+        if (r <= rb) {
+            if (r & 1) {
+                load_k_now(int_c<1>{}, kslot(tile_lo + r));
+                fast_step(int_c<1>{}, int_c<1>{}, tile_lo + r, false);
+                ++r;
+            } else {
+                load_k_now(int_c<0>{}, kslot(tile_lo + r));
+            }
+            for (; r + 1 <= rb; r += 2) {
+                fast_step(int_c<0>{}, int_c<1>{}, tile_lo + r, true);
+                fast_step(int_c<1>{}, int_c<1>{}, tile_lo + r + 1, false);
+            }
+            if (r <= rb) {
+                fast_step(int_c<0>{}, int_c<1>{}, tile_lo + r, true);
+                ++r;
+            }
+        }
+        for (; r <= ntiles; ++r) copy_step(r);
+    } else if (ntiles > 0) {
         // sets 0 .. STAGES-3; the first pair of steps reads sets 0 .. 2
         for (int s = tile_lo; s < tile_lo + T::STAGES - 2; ++s) issue(s);
         sync_pair();
@@ -677,10 +728,10 @@ void fa_fwd_kernel(FwdParams p) {
         int r = 0;
         for (; r < rf_lo || (r <= rf_hi && (r & 1)); ++r) step_masked(tile_lo + r, (r & 1) == 0);
         if (r + 1 <= rf_hi) {
-            load_k_now(kslot(tile_lo + r));
+            load_k_now(int_c<0>{}, kslot(tile_lo + r));
             for (; r + 1 <= rf_hi; r += 2) {
-                fast_step(int_c<0>{}, tile_lo + r, true);
-                fast_step(int_c<1>{}, tile_lo + r + 1, false);
+                fast_step(int_c<0>{}, int_c<0>{}, tile_lo + r, true);
+                fast_step(int_c<1>{}, int_c<0>{}, tile_lo + r + 1, false);
             }
         }
         for (; r <= ntiles; ++r) step_masked(tile_lo + r, (r & 1) == 0);
@@ -733,11 +784,11 @@ void fa_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, bool BF16, bool VARLEN, int MOD>
+template <int D, bool BF16, bool VARLEN, int MOD, bool BAND = false>
 static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
     const long long nblocks = (long long)p.nqt * (p.Hq / p.gw) * p.B;
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN, MOD>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN, MOD, BAND>), dim3((unsigned)nblocks),
                        dim3(kFwdThreads), 0, s, p);
     return hipGetLastError();
 }
@@ -748,7 +799,11 @@ static hipError_t launch_mod(const FwdParams& p, hipStream_t s) {
         case 1: return launch_one<D, BF16, false, 1>(p, s);
         case 2: return launch_one<D, BF16, false, 2>(p, s);
         case 3: return launch_one<D, BF16, false, 3>(p, s);
-        default: return launch_one<D, BF16, false, 0>(p, s);
+        default:
+            // a left window bounds every row's keys from below: the band
+            // form pays off (most computed steps cross a band edge)
+            if (p.wl >= 0) return launch_one<D, BF16, false, 0, true>(p, s);
+            return launch_one<D, BF16, false, 0>(p, s);
     }
 }
 
