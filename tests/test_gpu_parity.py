@@ -31,6 +31,12 @@ FWD_CASES = [
     ("window_left_only", 1, 2, 2, 260, 260, 128, "bf16", False, (70, -1), None, 110),
     ("window_right_only", 1, 2, 2, 260, 300, 128, "fp16", False, (-1, 40), None, 111),
     ("window_d64_causal", 2, 4, 2, 500, 500, 64, "bf16", True, (130, -1), None, 112),
+    # sliding windows take the band form of the kernel: also with Sq != Sk
+    # (the bottom-right alignment shifts the band) and a wide band over
+    # four query heads per work-group
+    ("window_sq_lt_sk", 1, 4, 2, 150, 420, 128, "bf16", True, (64, -1), None, 113),
+    ("window_sq_gt_sk_d64", 1, 4, 2, 420, 150, 64, "fp16", False, (40, 20), None, 114),
+    ("window_gqa_wide", 1, 8, 2, 600, 600, 128, "bf16", True, (300, -1), None, 115),
     ("negative_scale", 1, 2, 2, 150, 150, 128, "bf16", True, (-1, -1), -0.09, 113),
     ("zero_scale", 1, 2, 2, 150, 150, 128, "bf16", False, (-1, -1), 0.0, 114),
     ("single_query", 2, 8, 2, 1, 500, 128, "bf16", True, (-1, -1), None, 115),
