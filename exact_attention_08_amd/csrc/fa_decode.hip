@@ -355,8 +355,9 @@ void fa_decode_split_kernel(DecodeParams p) {
         red_s[wave][2][lq] = lr_tot;
     }
     __syncthreads();
-    // thread t: query t % 16, columns (t / 16) + 16*u
-    const int tq = threadIdx.x & 15, tc = threadIdx.x >> 4;
+    // thread t: query t / 16, columns t % 16 + 16*u (16 lanes store 64
+    // contiguous bytes of one partial row)
+    const int tq = threadIdx.x >> 4, tc = threadIdx.x & 15;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, red_s[w][0][tq]);
