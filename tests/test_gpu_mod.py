@@ -78,3 +78,29 @@ def test_no_modifier_is_the_plain_forward():
     o2, l2 = fa.fwd_mod(qd, kd, vd, causal=True, window=(30, -1))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 8, 2, 700, 700, 128, "bf16", True, (100, 0)),
+    (1, 4, 4, 530, 610, 64, "fp16", False, (90, 40)),
+], ids=["causal_gqa_d128", "two_sided_sq_lt_sk_d64"])
+def test_band_form_gives_the_plain_forms_bits(shape):
+    """A left window sends fa_fwd through the band form of the kernel (every
+    computed step in the interleaved pipeline); ALiBi with zero slopes runs
+    the modifier kernel, which uses the generic masked steps and, with zero
+    slopes, the plain arithmetic.  O must agree bit for bit (the same
+    weights and 16-bit sums in the same order); the fp32 row sums behind
+    LSE are added in a different tree order on masked steps, so LSE may
+    differ in its last bits."""
+    B, Hq, Hkv, Sq, Sk, d, dt, causal, window = shape
+    print(f"[case] band form vs generic form {shape}", flush=True)
+    q, k, v = synth.gen_padded(620, B, Hq, Hkv, Sq, Sk, d, dt)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o1, l1 = fa.fwd(qd, kd, vd, causal=causal, window=window)
+    o2, l2 = fa.fwd_mod(qd, kd, vd, causal=causal, window=window,
+                        alibi_slopes=torch.zeros(Hq, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(torch.isneginf(l1), torch.isneginf(l2))
+    fin = torch.isfinite(l1)
+    assert float((l1[fin] - l2[fin]).abs().max()) <= 4.0 * 2.0 ** -20 * max(1.0, float(l1[fin].abs().max()))
