@@ -13,6 +13,9 @@
 
 #include "fa_internal.hpp"
 
+static_assert(FA_DECODE_NOALLOC_MAX_BYTES == fa::kDecodeScratchBytes,
+              "the header states the scratch size of the allocation-free decode");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -82,6 +85,74 @@ fa_status_t check_seq_bytes(long long rows, int heads, int d, const char* what) 
         return fail(FA_ERR_UNSUPPORTED, "%s: %lld rows x %d heads x %d exceeds 2 GiB per sequence",
                     what, rows, heads, d);
     return FA_OK;
+}
+
+// Contiguous-cache decode.  With use_scratch the split partials go to the
+// library's per-GPU scratch array (fa_decode_kvcache_noalloc) instead of the
+// caller's workspace; every check still runs before any HIP call.
+fa_status_t decode_kvcache_impl(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_seqlens, void* out, float* lse, int B,
+                                int Hq, int Hkv, int Sk_cap, int max_seqlen_k, int d, int causal,
+                                int window_left, int window_right, float softmax_scale,
+                                int split_size, void* workspace, size_t workspace_bytes,
+                                bool use_scratch, fa_dtype_t dtype, hipStream_t stream) {
+    fa_status_t st = check_common(q, k_cache, v_cache, out, lse, B, Hq, Hkv, d, window_left,
+                                  window_right, softmax_scale, dtype);
+    if (st != FA_OK) return st;
+    if (!cache_seqlens || !aligned4(cache_seqlens))
+        return fail(FA_ERR_INVALID_ARG, "cache_seqlens must be non-null and 4-byte aligned");
+    if (Sk_cap < 1) return fail(FA_ERR_INVALID_ARG, "Sk_cap must be >= 1 (got %d)", Sk_cap);
+    if (max_seqlen_k < 1 || max_seqlen_k > Sk_cap)
+        return fail(FA_ERR_INVALID_ARG, "max_seqlen_k must be in [1, Sk_cap] (got %d)", max_seqlen_k);
+    if (split_size < 64 || split_size % 64 != 0)
+        return fail(FA_ERR_INVALID_ARG, "split_size must be a positive multiple of 64 (got %d)",
+                    split_size);
+    if ((st = check_seq_bytes(Sk_cap, Hkv, d, "k/v cache")) != FA_OK) return st;
+    const size_t need = fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d, split_size);
+    const int nsplit = (max_seqlen_k + split_size - 1) / split_size;
+    const int qblocks = (Hq / Hkv + 15) / 16;
+    if ((long long)nsplit * qblocks * Hkv * B * fa::kDecodeThreads > kMaxGridThreads)
+        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
+    if (use_scratch) {
+        if (need > fa::kDecodeScratchBytes)
+            return fail(FA_ERR_WORKSPACE,
+                        "partial results need %zu bytes, more than the %zu-byte scratch array of "
+                        "the allocation-free decode (use a larger split_size, fewer sequences, "
+                        "or fa_decode_kvcache with a workspace)",
+                        need, fa::kDecodeScratchBytes);
+        // the scratch address is per device: the stream must run on the
+        // current device, whose copy decode_scratch() returns
+        int cur = 0, sdev = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && stream != nullptr) e = hipStreamGetDevice(stream, &sdev);
+        else sdev = cur;
+        if (e != hipSuccess) return fail(FA_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+        if (sdev != cur)
+            return fail(FA_ERR_INVALID_ARG, "the stream belongs to device %d, not the current "
+                        "device %d", sdev, cur);
+        e = fa::decode_scratch(&workspace);
+        if (e != hipSuccess)
+            return fail(FA_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+        workspace_bytes = fa::kDecodeScratchBytes;
+    }
+    if (!workspace || !aligned16(workspace))
+        return fail(FA_ERR_WORKSPACE, "workspace must be non-null and 16-byte aligned");
+    if (workspace_bytes < need)
+        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+    fa::DecodeParams p{};
+    p.q = q; p.k = k_cache; p.v = v_cache; p.o = out; p.lse = lse;
+    p.seqlens = cache_seqlens;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
+    p.Sk_cap = Sk_cap;
+    p.max_len = max_seqlen_k;
+    p.split = split_size;
+    p.nsplit = nsplit;
+    p.qblocks = qblocks;
+    p.ws_o = static_cast<float*>(workspace);
+    p.ws_lse = p.ws_o + (size_t)B * Hq * p.nsplit * d;
+    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
+    set_scale(softmax_scale, &p.c, &p.qsign);
+    return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
 }
 
 }  // namespace
@@ -211,39 +282,20 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
                               int window_left, int window_right, float softmax_scale,
                               int split_size, void* workspace, size_t workspace_bytes,
                               fa_dtype_t dtype, hipStream_t stream) {
-    fa_status_t st = check_common(q, k_cache, v_cache, out, lse, B, Hq, Hkv, d, window_left,
-                                  window_right, softmax_scale, dtype);
-    if (st != FA_OK) return st;
-    if (!cache_seqlens || !aligned4(cache_seqlens))
-        return fail(FA_ERR_INVALID_ARG, "cache_seqlens must be non-null and 4-byte aligned");
-    if (Sk_cap < 1) return fail(FA_ERR_INVALID_ARG, "Sk_cap must be >= 1 (got %d)", Sk_cap);
-    if (max_seqlen_k < 1 || max_seqlen_k > Sk_cap)
-        return fail(FA_ERR_INVALID_ARG, "max_seqlen_k must be in [1, Sk_cap] (got %d)", max_seqlen_k);
-    if (split_size < 64 || split_size % 64 != 0)
-        return fail(FA_ERR_INVALID_ARG, "split_size must be a positive multiple of 64 (got %d)",
-                    split_size);
-    if ((st = check_seq_bytes(Sk_cap, Hkv, d, "k/v cache")) != FA_OK) return st;
-    const size_t need = fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d, split_size);
-    if (!workspace || !aligned16(workspace))
-        return fail(FA_ERR_WORKSPACE, "workspace must be non-null and 16-byte aligned");
-    if (workspace_bytes < need)
-        return fail(FA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
-    fa::DecodeParams p{};
-    p.q = q; p.k = k_cache; p.v = v_cache; p.o = out; p.lse = lse;
-    p.seqlens = cache_seqlens;
-    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
-    p.Sk_cap = Sk_cap;
-    p.max_len = max_seqlen_k;
-    p.split = split_size;
-    p.nsplit = (max_seqlen_k + split_size - 1) / split_size;
-    p.qblocks = (p.G + 15) / 16;
-    p.ws_o = static_cast<float*>(workspace);
-    p.ws_lse = p.ws_o + (size_t)B * Hq * p.nsplit * d;
-    p.causal = causal ? 1 : 0; p.wl = window_left; p.wr = window_right;
-    set_scale(softmax_scale, &p.c, &p.qsign);
-    if ((long long)p.nsplit * p.qblocks * Hkv * B * fa::kDecodeThreads > kMaxGridThreads)
-        return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
-    return launch_status(fa::launch_decode(p, d, dtype == FA_BF16, stream));
+    return decode_kvcache_impl(q, k_cache, v_cache, cache_seqlens, out, lse, B, Hq, Hkv, Sk_cap,
+                               max_seqlen_k, d, causal, window_left, window_right, softmax_scale,
+                               split_size, workspace, workspace_bytes, false, dtype, stream);
+}
+
+fa_status_t fa_decode_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* cache_seqlens, void* out, float* lse, int B,
+                                      int Hq, int Hkv, int Sk_cap, int max_seqlen_k, int d,
+                                      int causal, int window_left, int window_right,
+                                      float softmax_scale, int split_size, fa_dtype_t dtype,
+                                      hipStream_t stream) {
+    return decode_kvcache_impl(q, k_cache, v_cache, cache_seqlens, out, lse, B, Hq, Hkv, Sk_cap,
+                               max_seqlen_k, d, causal, window_left, window_right, softmax_scale,
+                               split_size, nullptr, 0, true, dtype, stream);
 }
 
 fa_status_t fa_decode_paged(const void* q, void* k_pages, void* v_pages,

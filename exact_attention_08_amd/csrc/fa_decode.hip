@@ -42,6 +42,8 @@
 // With an append, a small kernel first writes the new token's key and value
 // row at position cache_seqlens[b], and the split and combine kernels see
 // one more key.
+#include <mutex>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -478,6 +480,35 @@ static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t s) {
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s) {
     if (d == 128) return bf16 ? launch_decode_t<128, true>(p, s) : launch_decode_t<128, false>(p, s);
     return bf16 ? launch_decode_t<64, true>(p, s) : launch_decode_t<64, false>(p, s);
+}
+
+// Split partials of the allocation-free decode entry point.  Every GPU the
+// library runs on holds its own copy until the process ends, and every such
+// call on that GPU shares it, so calls that overlap on one GPU race.
+// Nothing in it needs to start at zero: the split kernel writes every
+// partial row and LSE that the combine kernel then reads.  Host code must
+// not pass this name to a kernel (on the host it is only a stand-in): the
+// device address comes from decode_scratch().
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+hipError_t decode_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // with this device current: its own copy of the array
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 }  // namespace fa

@@ -115,6 +115,13 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStre
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, bool bf16, hipStream_t s);
 
+// Allocation-free decode: the split partials go to a fixed device array of
+// this many bytes (one per GPU, alive until the process ends) instead of a
+// caller workspace.  decode_scratch() returns that array's device address on
+// the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Kernel tile geometry, shared with the host for grid sizing.
 constexpr int kFwdWaveRows = 64;   // query rows per forward wave
 constexpr int kFwdWaves = 4;       // waves per forward work-group (one per SIMD)

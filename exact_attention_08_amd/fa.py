@@ -24,7 +24,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_INVALID_ARG", 2: "FA_ERR_UNSUPPORTED", 3: "FA_E
 
 # Every symbol include/fa.h declares.
 EXPORTS = ("fa_fwd", "fa_fwd_mod", "fa_fwd_fp8_workspace_bytes", "fa_fwd_fp8", "fa_fwd_varlen", "fa_decode_workspace_bytes", "fa_decode_kvcache",
-           "fa_decode_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
+           "fa_decode_kvcache_noalloc", "fa_decode_paged", "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
            "fa_last_error")
 
 _lock = threading.Lock()
@@ -67,6 +67,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_decode_kvcache.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P,
                                           ctypes.c_size_t, I, P]
         lib.fa_decode_kvcache.restype = I
+        lib.fa_decode_kvcache_noalloc.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F,
+                                                  I, I, P]
+        lib.fa_decode_kvcache_noalloc.restype = I
         lib.fa_decode_paged.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, I,
                                         F, I, P, ctypes.c_size_t, I, P]
         lib.fa_decode_paged.restype = I
@@ -242,6 +245,33 @@ def decode_kvcache(q, k_cache, v_cache, cache_seqlens, max_seqlen_k, *, causal=F
                                  _scale(softmax_scale, d), int(split_size), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(),
                                  _DTYPE[q.dtype], _stream()))
+    return out, lse
+
+
+# Largest partial-result size of decode_kvcache_noalloc (FA_DECODE_NOALLOC_MAX_BYTES).
+DECODE_NOALLOC_MAX_BYTES = 64 << 20
+
+
+def decode_kvcache_noalloc(q, k_cache, v_cache, cache_seqlens, max_seqlen_k, *, out, lse=None,
+                           causal=False, window=(-1, -1), softmax_scale=None, split_size=1024):
+    """decode_kvcache without a workspace: the library keeps the split partials in its
+    own per-GPU scratch array (for callers that cannot allocate).  The caller passes
+    out (and lse, or None); this function allocates nothing."""
+    _check_tensors(q, k_cache, v_cache, out)
+    _require(q.dim() == 4 and q.shape[1] == 1, "q must be [B,1,Hq,d]")
+    _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "caches must be [B,Sk_cap,Hkv,d]")
+    _require(out.shape == q.shape, "out must be shaped like q")
+    _require(cache_seqlens.is_cuda and cache_seqlens.dtype == torch.int32,
+             "cache_seqlens must be an int32 GPU vector")
+    B, _, Hq, d = q.shape
+    _, Sk_cap, Hkv, _ = k_cache.shape
+    if lse is not None:
+        _require(lse.is_cuda and lse.dtype == torch.float32 and lse.is_contiguous()
+                 and tuple(lse.shape) == (B, Hq), "lse must be a contiguous fp32 [B,Hq] GPU tensor")
+    _check(load().fa_decode_kvcache_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Hq,
+        Hkv, Sk_cap, int(max_seqlen_k), d, int(bool(causal)), int(window[0]), int(window[1]),
+        _scale(softmax_scale, d), int(split_size), _DTYPE[q.dtype], _stream()))
     return out, lse
 
 

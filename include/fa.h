@@ -182,6 +182,34 @@ fa_status_t fa_decode_kvcache(const void* q, const void* k_cache, const void* v_
                               void* workspace, size_t workspace_bytes,
                               fa_dtype_t dtype, hipStream_t stream);
 
+/* Largest partial-result size, in bytes, of fa_decode_kvcache_noalloc:
+ * fa_decode_workspace_bytes(B, Hq, max_seqlen_k, d, split_size) must not
+ * exceed it (64 MiB: e.g. 64 sequences x 32 query heads x 31 splits at
+ * d = 128). */
+#define FA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
+/* fa_decode_kvcache for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, layouts, results and errors as
+ * fa_decode_kvcache, without the workspace: the split partials go to a
+ * scratch array inside the library, FA_DECODE_NOALLOC_MAX_BYTES per GPU,
+ * which every GPU the library runs on holds until the process ends.  The
+ * call itself allocates nothing (its first call on a device looks up that
+ * device's array address once).
+ *   - Sizes whose partials exceed FA_DECODE_NOALLOC_MAX_BYTES are rejected
+ *     with FA_ERR_WORKSPACE before anything is enqueued.
+ *   - `stream` must belong to the current device (else FA_ERR_INVALID_ARG).
+ *   - All such calls on one GPU share its array: calls that overlap in time
+ *     on one GPU (on different streams, or from different threads without
+ *     ordering) race and may return wrong results.  Calls ordered on one
+ *     stream are safe; nothing in the array has to start at zero. */
+fa_status_t fa_decode_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* cache_seqlens, void* out, float* lse,
+                                      int B, int Hq, int Hkv, int Sk_cap, int max_seqlen_k, int d,
+                                      int causal, int window_left, int window_right,
+                                      float softmax_scale, int split_size,
+                                      fa_dtype_t dtype, hipStream_t stream);
+
 /* One-token decode against a PAGED KV cache, optionally appending the new
  * token's key and value first ("FlashAttention" project summary, feature
  * list: the cached-decode call with paged KV cache support; explainer page,

@@ -35,7 +35,8 @@ def test_header_declares_expected_api():
     assert declared_functions() == sorted(["fa_fwd", "fa_fwd_mod", "fa_fwd_fp8_workspace_bytes",
                                            "fa_fwd_fp8", "fa_fwd_varlen",
                                            "fa_decode_workspace_bytes",
-                                           "fa_decode_kvcache", "fa_decode_paged",
+                                           "fa_decode_kvcache", "fa_decode_kvcache_noalloc",
+                                           "fa_decode_paged",
                                            "fa_bwd_workspace_bytes", "fa_bwd", "fa_status_str",
                                            "fa_last_error"])
 
@@ -181,6 +182,33 @@ def test_workspace_exact_boundary(lib):
     need = lib.fa_decode_workspace_bytes(2, 8, 4096, 128, 1024)
     assert decode(lib, ws_bytes=need - 1) == 3
     assert "workspace too small" in lib.fa_last_error().decode()
+
+
+def decode_noalloc(lib, B=2, Hq=8, Hkv=2, cap=4096, maxk=4096, d=128, split=1024,
+                   seqlens=FAKE, dtype=0):
+    return lib.fa_decode_kvcache_noalloc(FAKE, FAKE, FAKE, seqlens, FAKE, FAKE, B, Hq, Hkv, cap,
+                                         maxk, d, 1, -1, -1, 0.1, split, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seqlens=None), 1), (dict(cap=0), 1), (dict(maxk=0), 1), (dict(maxk=5000), 1),
+    (dict(split=100), 1), (dict(d=32), 2), (dict(Hq=7), 1), (dict(dtype=3), 2),
+    # partials beyond the 64 MiB scratch array: 64 x 32 x 64 splits x 129 x 4 B
+    (dict(B=64, Hq=32, Hkv=8, cap=65536, maxk=65536), 3),
+])
+def test_decode_noalloc_rejects_on_the_host(lib, kw, status):
+    assert decode_noalloc(lib, **kw) == status
+    if status == 3:
+        assert "scratch" in lib.fa_last_error().decode()
+
+
+def test_decode_noalloc_limit_matches_header(lib):
+    from exact_attention_08_amd import fa
+    text = open(HEADER).read()
+    assert "#define FA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)" in text
+    assert fa.DECODE_NOALLOC_MAX_BYTES == 64 << 20
+    # the largest benchmark decode (64 x 32 heads, 32768 keys, 1024-key splits) fits
+    assert lib.fa_decode_workspace_bytes(64, 32, 32768, 128, 1024) <= fa.DECODE_NOALLOC_MAX_BYTES
 
 
 def paged(lib, kp=FAKE, table=FAKE, seqlens=FAKE, kn=None, vn=None, ws=FAKE, ws_bytes=1 << 30,
