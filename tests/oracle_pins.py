@@ -772,6 +772,62 @@ def pin_fp8_attention(orc):
         assert abs(lz[0, 0, i] - math.log(i + Sk - Sq + 1)) < 1e-13
 
 
+# -- the row-sampled entry (used by the full-size GPU checks) ----------------
+_ROW_CASES = [  # Sq, Sk, causal, wl, wr: every mask mode the sampled checks use
+    (40, 40, False, -1, -1), (40, 40, True, -1, -1), (40, 40, True, 7, -1),
+    (40, 40, True, 7, 7), (40, 40, False, 5, 9), (25, 40, True, -1, -1),
+    (40, 25, True, -1, -1), (30, 45, True, 6, 0), (45, 30, False, 4, 2),
+]
+
+
+def _unsorted_rows(rng, Sq):
+    """Row indices in no particular order: both ends, a repeat and random rows."""
+    qi = np.concatenate([[Sq - 1, 0], rng.integers(0, Sq, 9), [Sq // 2, Sq // 2]])
+    return rng.permutation(qi)
+
+
+def pin_rows_match_sdpa_masked(orc):
+    """attention_rows on unsorted row indices equals torch float64 SDPA (mask
+    built from torch band helpers) row by row, in every mask mode and with
+    Sq < Sk and Sq > Sk (bottom-right alignment)."""
+    rng = _rng(31)
+    for (Sq, Sk, causal, wl, wr) in _ROW_CASES:
+        d = 5
+        q = _rand(rng, 1, Sq, 1, d); k = _rand(rng, 1, Sk, 1, d); v = _rand(rng, 1, Sk, 1, d)
+        ro, rl = _sdpa_reference(q, k, v, causal, wl, wr, 0.6)
+        qi = _unsorted_rows(rng, Sq)
+        o, l = orc.attention_rows(q[0, qi, 0], qi, Sq, k[0, :, 0], v[0, :, 0], causal=causal,
+                                  window=(wl, wr), scale=0.6)
+        for r, i in enumerate(qi):
+            if np.isneginf(rl[0, 0, i]):          # no visible key: O = 0, LSE = -inf
+                assert np.isneginf(l[r]) and np.all(o[r] == 0.0), (Sq, Sk, causal, wl, wr, i)
+                continue
+            assert abs(l[r] - rl[0, 0, i]) < 1e-12, (Sq, Sk, causal, wl, wr, i)
+            assert np.abs(o[r] - ro[0, i, 0]).max() < 1e-12, (Sq, Sk, causal, wl, wr, i)
+
+
+def pin_rows_zero_query_closed_form(orc):
+    """attention_rows with Q = 0: LSE of sampled row i = ln(#visible keys of
+    row i), O = mean of those value rows; includes the decode form (one
+    query at the last position of its cache) and unsorted indices."""
+    rng = _rng(32)
+    cases = _ROW_CASES + [(1, 37, True, -1, -1), (1, 37, False, 10, -1)]
+    for (Sq, Sk, causal, wl, wr) in cases:
+        d = 4
+        k = _rand(rng, Sk, d); v = _rand(rng, Sk, d)
+        qi = _unsorted_rows(rng, Sq)
+        o, l = orc.attention_rows(np.zeros((len(qi), d)), qi, Sq, k, v, causal=causal,
+                                  window=(wl, wr), scale=1.3)
+        for r, i in enumerate(qi):
+            lo, hi = _interval(int(i), Sq, Sk, causal, wl, wr)
+            lo = max(lo, 0)
+            if hi < lo:
+                assert np.isneginf(l[r]) and np.all(o[r] == 0.0)
+                continue
+            assert abs(l[r] - math.log(hi - lo + 1)) < 1e-13, (Sq, Sk, causal, wl, wr, i)
+            assert np.abs(o[r] - v[lo:hi + 1].mean(0)).max() < 1e-13
+
+
 PINS = [
     pin_worked_example, pin_torch_sdpa, pin_zero_query_closed_form, pin_varlen_zero_query,
     pin_decode_zero_query, pin_constant_v, pin_single_visible_key, pin_one_hot_values,
@@ -782,4 +838,5 @@ PINS = [
     pin_bwd_gqa_equals_repeated_mha, pin_paged_equals_contiguous, pin_paged_append,
     pin_paged_append_zero_query, pin_mod_torch_reference, pin_mod_neutral,
     pin_alibi_zero_query_closed_form, pin_softcap_saturates, pin_e4m3_decoder, pin_fp8_attention,
+    pin_rows_match_sdpa_masked, pin_rows_zero_query_closed_form,
 ]
