@@ -169,6 +169,11 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     if (Sq == 0) return ok();
     if ((st = check_seq_bytes(Sq, Hq, d, "q")) != FA_OK) return st;
     if ((st = check_seq_bytes(Sk, Hkv, d, "k/v")) != FA_OK) return st;
+    // A window bound that cuts no row is no bound (row positions run from
+    // Sk - Sq to Sk - 1): dropping it keeps the plain kernel form, which is
+    // faster where few steps cross a band edge.
+    if (window_left >= Sk - 1) window_left = -1;
+    if (window_right >= Sq - 1) window_right = -1;
     fa::FwdParams p{};
     p.q = q; p.k = k; p.v = v; p.o = out; p.lse = lse;
     p.cu_q = nullptr; p.cu_k = nullptr;
@@ -457,8 +462,7 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* out,
     const int bmq = 32 * fa::bwd_dq_waves(d) / p.gw;
     p.nqb = (Sq + bmq - 1) / bmq;
     if ((long long)p.nkb * Hkv * B * 64 * fa::kBwdDkdvWaves > kMaxGridThreads ||
-        (long long)p.nqb * (Hq / p.gw) * B * 64 * fa::bwd_dq_waves(d) > kMaxGridThreads ||
-        (long long)B * Sq * Hq * (d / 8) > kMaxGridThreads)
+        (long long)p.nqb * (Hq / p.gw) * B * 64 * fa::bwd_dq_waves(d) > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
     return launch_status(fa::launch_bwd(p, d, dtype == FA_BF16, stream));
 }

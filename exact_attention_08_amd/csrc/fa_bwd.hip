@@ -45,7 +45,7 @@
 
 namespace fa {
 
-template <int D, int WAVES = kBwdWaves>
+template <int D, int WAVES>
 struct BwdGeo {
     static constexpr int R = 32;                 // rows (or keys) per tile and per wave
     static constexpr int NW = WAVES;             // waves per work-group

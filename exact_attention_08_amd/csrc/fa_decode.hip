@@ -359,6 +359,7 @@ void fa_decode_split_kernel(DecodeParams p) {
     __syncthreads();
     // thread t: query t / 16, columns t % 16 + 16*u (16 lanes store 64
     // contiguous bytes of one partial row)
+    static_assert(NW * 64 == 16 * 16, "the merge maps the work-group's threads to 16 queries x 16 columns");
     const int tq = threadIdx.x >> 4, tc = threadIdx.x & 15;
     float M = -INFINITY;
 #pragma unroll

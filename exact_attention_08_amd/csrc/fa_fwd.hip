@@ -800,8 +800,9 @@ static hipError_t launch_mod(const FwdParams& p, hipStream_t s) {
         case 2: return launch_one<D, BF16, false, 2>(p, s);
         case 3: return launch_one<D, BF16, false, 3>(p, s);
         default:
-            // a left window bounds every row's keys from below: the band
-            // form pays off (most computed steps cross a band edge)
+            // a left window that cuts rows (the host drops one that cuts
+            // none) bounds every row's keys from below: the band form pays
+            // off (most computed steps cross a band edge)
             if (p.wl >= 0) return launch_one<D, BF16, false, 0, true>(p, s);
             return launch_one<D, BF16, false, 0>(p, s);
     }

@@ -1,5 +1,5 @@
 // fa_internal.hpp -- parameter blocks shared by the host launcher (fa_api.cpp)
-// and the kernels (fa_fwd.hip, fa_decode.hip).  Host-side only types.
+// and the kernels (fa_fwd.hip, fa_fwd_fp8.hip, fa_decode.hip, fa_bwd.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -85,7 +85,8 @@ struct DecodeParams {
     const void* v_new;
 };
 
-// Backward (gradients): row-term kernel, dK/dV kernel, dQ kernel.
+// Backward (gradients): the dQ kernel (which also forms the row terms D and
+// the LSE in log2 units), then the dK/dV kernel.
 struct BwdParams {
     const void* q;
     const void* k;
@@ -105,9 +106,9 @@ struct BwdParams {
     int causal, wl, wr;
     float scale;                // softmax scale (any sign)
     float c2;                   // scale * log2(e)
-    int nkb;                    // 128-key blocks per (sequence, K/V head)
+    int nkb;                    // kBwdKeysPerWg-key blocks per (sequence, K/V head)
     int gw;                     // query heads per dQ work-group
-    int nqb;                    // query blocks of 128/gw rows per (sequence, head group)
+    int nqb;                    // query blocks of 32*bwd_dq_waves(d)/gw rows per (sequence, head group)
 };
 
 // Host launchers (defined next to their kernels).
@@ -134,8 +135,6 @@ inline int fwd_rows_per_wg(int G) { return kFwdWaveRows * kFwdWaves / fwd_heads_
 constexpr int kDecodeWaves = 4;    // waves per decode split work-group
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr float kLog2e_host = 1.4426950408889634f;
-constexpr int kBwdWaves = 4;       // waves per backward work-group
-constexpr int kBwdThreads = 64 * kBwdWaves;
 // dQ work-group: 32 rows per wave, two waves per SIMD; 8 waves split the
 // three 8 KB tiles of a d = 128 stage evenly, 4 those of d = 64
 constexpr int bwd_dq_waves(int d) { return d == 128 ? 8 : 4; }

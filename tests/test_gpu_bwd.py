@@ -14,6 +14,8 @@ import torch
 
 import oracle
 from exact_attention_08_amd import fa, synth
+from oracle.checks import check_grad as check
+from oracle.checks import grad_error_bounds as error_bounds
 
 pytestmark = pytest.mark.gpu
 
@@ -39,70 +41,6 @@ BWD_CASES = [
     ("group3_window_left", 1, 6, 2, 260, 260, 128, "bf16", True, (64, -1), None, 216),
     ("group6_d64_fp16", 1, 6, 1, 300, 333, 64, "fp16", False, (-1, -1), None, 217),
 ]
-
-
-def error_bounds(q, k, v, go, causal, window, scale):
-    """Per-element error bounds of the three gradients (tolerances only; the
-    expected values come from the oracle).
-
-    Each gradient element is a sum over rows or keys:
-        dV_jc = sum_i P_ij dO_ic,   dK_jc = scale sum_i dS_ij Q_ic,
-        dQ_ic = scale sum_j dS_ij K_jc,   dS_ij = P_ij (dP_ij - D_i),
-    and the kernels round P and dS to the input dtype before these products
-    (relative error <= 2^-9 per term; 2^-12 for fp16).  Under cancellation
-    the error is relative to the sum of the absolute terms A, not to the
-    result, so the bound is 2^-8 * A (a 2x margin), A summed here in fp64
-    with P, dP and dS written out per head.
-    The row term D_i = dO_i . O_i is formed from the forward's 16-bit output,
-    so each dS_ij of row i carries an error dD_i <= E_i =
-    2^-7 sum_c |dO_ic| (|O_ic| + 2^-7) (output rounding 2^-9 |O| plus the
-    forward's own error); it adds scale E_i |sum_j P_ij K_jc| to dQ and
-    scale sum_i P_ij E_i |Q_ic| to dK.  The final rounding of each gradient
-    to the input dtype adds 2^-8 |g| (in ``check``)."""
-    from oracle_pins import _visible_band
-    sc = scale if scale is not None else q.shape[-1] ** -0.5
-    qf, kf, vf, gf = (x.double().numpy() for x in (q, k, v, go))
-    B, Sq, Hq, d = qf.shape
-    Sk, Hkv = kf.shape[1], kf.shape[2]
-    G = Hq // Hkv
-    vis = _visible_band(Sq, Sk, causal, window[0], window[1]).numpy()
-    bq, bk, bv = np.zeros_like(qf), np.zeros_like(kf), np.zeros_like(vf)
-    for b in range(B):
-        for h in range(Hq):
-            g = h // G
-            s = np.where(vis, sc * qf[b, :, h] @ kf[b, :, g].T, -np.inf)
-            m = s.max(1, keepdims=True)
-            m[~np.isfinite(m)] = 0.0
-            e = np.where(vis, np.exp(s - m), 0.0)
-            z = e.sum(1, keepdims=True)
-            P = e / np.where(z > 0, z, 1.0)
-            dO = gf[b, :, h]
-            O = P @ vf[b, :, g]
-            dP = dO @ vf[b, :, g].T
-            D = (dO * O).sum(1, keepdims=True)
-            aS = np.abs(P * (dP - D))
-            E = 2.0 ** -7 * (np.abs(dO) * (np.abs(O) + 2.0 ** -7)).sum(1, keepdims=True)
-            bv[b, :, g] += 2.0 ** -8 * (P.T @ np.abs(dO))
-            bk[b, :, g] += abs(sc) * (2.0 ** -8 * (aS.T @ np.abs(qf[b, :, h])) + P.T @ (E * np.abs(qf[b, :, h])))
-            bq[b, :, h] = abs(sc) * (2.0 ** -8 * (aS @ np.abs(kf[b, :, g])) + E * np.abs(P @ kf[b, :, g]))
-    return bq, bk, bv
-
-
-def check(name, got, ref, extra):
-    g = got.detach().to("cpu", torch.float64).numpy()
-    assert g.shape == ref.shape, (name, g.shape, ref.shape)
-    assert np.isfinite(g).all(), f"{name}: non-finite gradient"
-    err = np.abs(g - ref)
-    tol = 2.0 ** -8 * np.abs(ref) + extra
-    bad = err > tol
-    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
-    if ref.size:
-        w = int(np.argmax(err / np.maximum(tol, 1e-300)))
-        worst = float(err.reshape(-1)[w] / max(tol.reshape(-1)[w], 1e-300))
-        print(f"[grad] {name}: max|err| {err.max():.3e}  rms(ref) {rms:.3e}  worst err/tol "
-              f"{worst:.3f} at ref {ref.reshape(-1)[w]:.4e} got {g.reshape(-1)[w]:.4e} "
-              f"(index {np.unravel_index(w, ref.shape)})", flush=True)
-    assert not bad.any(), f"{name}: {int(bad.sum())} elements exceed the tolerance"
 
 
 def run_case(case):

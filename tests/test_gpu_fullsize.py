@@ -1,25 +1,30 @@
-"""Parity at the benchmark workloads' full sizes, in the same launch
-configuration the benchmark times: sampled output rows against the fp64
-oracle computed one by one (all rows for the decode workload), plus
-properties that hold at any size (finite outputs; each output row is a
-convex combination of visible value rows, so it lies inside their range;
-LSE is at least the score of any visible key)."""
+"""Parity at the benchmark workloads' full sizes, in the launch configuration
+the benchmark times, against the fp64 oracle:
+
+  * causal GQA prefill, causal sliding window and the packed (varlen)
+    workload: EVERY output row of every head and sequence is compared;
+  * the 65,536-token causal prefill: all 32 heads, the first and last 512
+    rows and every 32nd row between (the oracle needs ~3.5e13 fp64 FLOP for
+    all of it; this sample covers the shortest rows, the longest rows and a
+    stride through the middle, ~1/20 of the work);
+  * the KV-cache decode: every (sequence, query head).
+
+Each check prints max |dO|, max |dLSE|, the count of elements above 1e-2
+(accepted only within one output ulp of an exact value of magnitude >= 2,
+see oracle/checks.py), the rounding floor of the output format and the
+largest distance of a GPU value from the correctly rounded exact value.  Properties that hold at any size are checked on the whole output as
+well (finite values; each output row lies inside the range of its K/V
+head's values; LSE is at least the diagonal key's score)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from exact_attention_08_amd import fa, synth
-from parity_util import compare, log
+from oracle.checks import compare, log, merge
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-
-
-def _sample_rows(rng, S, n):
-    fixed = [0, 1, 63, 64, 127, 128, 129, S // 2, S - 129, S - 128, S - 1]
-    rows = [r for r in fixed if 0 <= r < S] + list(rng.integers(0, S, n))
-    return sorted(set(int(r) for r in rows))
 
 
 def _range_check(o, v, G):
@@ -30,7 +35,7 @@ def _range_check(o, v, G):
     assert torch.all(of >= vmin[:, None] - 1e-2) and torch.all(of <= vmax[:, None] + 1e-2)
 
 
-def _check_padded(w):
+def _run_padded(w):
     q, k, v = synth.generate(w)
     print(f"[case] full-size {w.name}", flush=True)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
@@ -42,32 +47,60 @@ def _check_padded(w):
     # LSE_i >= scale * q_i . k_i (the diagonal key is visible in these workloads)
     s_diag = (qd.float() * kd.repeat_interleave(G, dim=2).float()).sum(-1) * w.scale  # [B,S,Hq]
     assert torch.all(lse.permute(0, 2, 1) >= s_diag - 1e-3)
-    rng = np.random.default_rng(w.seed)
-    o_c, l_c = o.cpu(), lse.cpu()
-    stats = []
-    heads = sorted(set([0, w.Hq - 1] + list(rng.integers(0, w.Hq, 4))))
-    for b in sorted(set([0, w.B - 1])):
-        for h in heads:
-            rows = _sample_rows(rng, w.Sq, 12)
-            g = h // G
-            ro, rl = oracle.attention_rows(q[b, rows, h], rows, w.Sq, k[b, :, g], v[b, :, g],
-                                           causal=w.causal, window=w.window, scale=w.scale)
-            stats.append(compare(o_c[b, rows, h], l_c[b, h, rows], ro, rl, w.dtype,
-                                 f"{w.name} b{b} h{h}"))
-    log({"max_dO": max(s["max_dO"] for s in stats), "max_dLSE": max(s["max_dLSE"] for s in stats),
-         "rows": sum(s["n"] for s in stats) // w.d}, w.name)
+    return (q, k, v), (o, lse), (qd, kd, vd)
+
+
+def _check_all_rows(w):
+    (q, k, v), (o, lse), _ = _run_padded(w)
+    ro, rl = oracle.attention(q, k, v, causal=w.causal, window=w.window, scale=w.scale)
+    stats = compare(o.cpu(), lse.cpu(), ro, rl, w.dtype, w.name)
+    stats["rows"] = stats.pop("n") // w.d
+    log(stats, w.name + " (all rows)")
 
 
 def test_causal_gqa_prefill_full():
-    _check_padded(synth.WORKLOADS["causal_gqa_prefill"])
+    _check_all_rows(synth.WORKLOADS["causal_gqa_prefill"])
 
 
 def test_causal_window_full():
-    _check_padded(synth.WORKLOADS["causal_window"])
+    _check_all_rows(synth.WORKLOADS["causal_window"])
 
 
-def test_long_causal_prefill_full():
-    _check_padded(synth.WORKLOADS["long_causal_prefill"])
+def test_causal_window_band_form_equals_generic_form():
+    """At the sliding-window workload's full shape the band form (every step
+    in the interleaved pipeline, masks applied at region starts) gives the
+    same O bits as the generic masked-step form (reached through the score
+    modifier entry with zero ALiBi slopes, which keeps the plain order of
+    maxima); LSE may differ in its last bits (another fp32 summation tree)."""
+    w = synth.WORKLOADS["causal_window"]
+    _, (o, lse), (qd, kd, vd) = _run_padded(w)
+    zero = torch.zeros(w.Hq, dtype=torch.float32, device=DEV)
+    o2, lse2 = fa.fwd_mod(qd, kd, vd, causal=w.causal, window=w.window, alibi_slopes=zero)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    rel = ((lse - lse2).abs() / lse2.abs().clamp_min(1.0)).max().item()
+    print(f"[parity] {w.name}: band vs generic form: O bitwise equal, max rel dLSE {rel:.3g}",
+          flush=True)
+    assert rel <= 4 * 2.0 ** -23
+
+
+def test_long_causal_prefill_rows():
+    w = synth.WORKLOADS["long_causal_prefill"]
+    (q, k, v), (o, lse), _ = _run_padded(w)
+    S, G = w.Sq, w.Hq // w.Hkv
+    rows = np.unique(np.concatenate([np.arange(512), np.arange(S - 512, S),
+                                     np.arange(512, S - 512, 32)]))
+    o_c, l_c = o.cpu(), lse.cpu()
+    stats = []
+    for h in range(w.Hq):
+        g = h // G
+        ro, rl = oracle.attention_rows(q[0, rows, h], rows, S, k[0, :, g], v[0, :, g],
+                                       causal=True, scale=w.scale)
+        stats.append(compare(o_c[0, rows, h], l_c[0, h, rows], ro, rl, w.dtype,
+                             f"{w.name} h{h}"))
+    m = merge(stats)
+    m["rows"] = m.pop("n") // w.d
+    log(m, f"{w.name} (all {w.Hq} heads x {len(rows)} rows)")
 
 
 def test_varlen_causal_full():
@@ -79,21 +112,10 @@ def test_varlen_causal_full():
     o, lse = fa.fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV), cud, cud, mx, mx, causal=True)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    rng = np.random.default_rng(w.seed)
-    G = w.Hq // w.Hkv
-    o_c, l_c = o.cpu(), lse.cpu()
-    stats = []
-    for z in range(w.B):
-        a, L = int(cu[z]), int(lens[z])
-        rows = sorted(set([0, L - 1] + list(rng.integers(0, L, 3))))
-        for h in (int(rng.integers(0, w.Hq)),):
-            g = h // G
-            ro, rl = oracle.attention_rows(q[a + np.array(rows), h], rows, L, k[a:a + L, g],
-                                           v[a:a + L, g], causal=True, scale=w.scale)
-            stats.append(compare(o_c[a + np.array(rows), h], l_c[h, a + np.array(rows)], ro, rl,
-                                 w.dtype, f"{w.name} z{z} h{h}"))
-    log({"max_dO": max(s["max_dO"] for s in stats), "max_dLSE": max(s["max_dLSE"] for s in stats),
-         "rows": sum(s["n"] for s in stats) // w.d}, w.name)
+    ro, rl = oracle.attention_varlen(q, k, v, cu, cu, causal=True, scale=w.scale)
+    stats = compare(o.cpu(), lse.cpu(), ro, rl, w.dtype, w.name)
+    stats["rows"] = stats.pop("n") // w.d
+    log(stats, w.name + " (all rows)")
 
 
 def test_kvcache_decode_full():
@@ -115,5 +137,6 @@ def test_kvcache_decode_full():
             ro, rl = oracle.attention_rows(q[b, 0, hs], [L - 1] * G, L, kc[b, :L, g], vc[b, :L, g],
                                            causal=True, scale=w.scale)
             stats.append(compare(o_c[b, 0, hs], l_c[b, hs], ro, rl, w.dtype, f"{w.name} b{b} g{g}"))
-    log({"max_dO": max(s["max_dO"] for s in stats), "max_dLSE": max(s["max_dLSE"] for s in stats),
-         "rows": sum(s["n"] for s in stats) // w.d}, w.name)
+    m = merge(stats)
+    m["rows"] = m.pop("n") // w.d
+    log(m, f"{w.name} (every sequence and head)")

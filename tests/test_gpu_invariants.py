@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from exact_attention_08_amd import fa, synth
-from parity_util import compare
+from oracle.checks import compare
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"

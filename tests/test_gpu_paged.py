@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from exact_attention_08_amd import fa, synth
-from parity_util import compare, log
+from oracle.checks import compare, log
 
 pytestmark = pytest.mark.gpu
 

@@ -4,13 +4,13 @@ tails, plus the degenerate cases (empty key sets, single key, single query,
 fully masked rows, zero and negative scale).
 
 Tolerance: max |dO| <= 1e-2, max |dLSE| <= 1e-3 against the unrounded fp64
-oracle (see parity_util for the one-ulp rule on |O| >= 2)."""
+oracle (see oracle/checks.py for the one-ulp rule on |O| >= 2)."""
 import pytest
 import torch
 
 import oracle
 from exact_attention_08_amd import fa, synth
-from parity_util import compare, log
+from oracle.checks import compare, log
 
 pytestmark = pytest.mark.gpu
 
