@@ -17,12 +17,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa355.so")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_wide.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
 # MFMA results of the forward kernel are consumed by VALU code (the softmax):
 # keep them in arch VGPRs instead of accumulation registers.  Its arithmetic
 # never makes a NaN from finite inputs, so NaNs need not be honoured: v_max
 # then takes MFMA results directly instead of after a quieting copy each.
 EXTRA = {"fa_fwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+         "fa_fwd_wide.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
          "fa_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

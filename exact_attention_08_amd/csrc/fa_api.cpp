@@ -179,8 +179,9 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     p.cu_q = nullptr; p.cu_k = nullptr;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk;
+    const bool wide = fa::fwd_use_wide(Sk, causal, window_left, window_right);
     p.gw = fa::fwd_heads_per_wg(p.G);
-    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G, wide ? fa::kFwdWideWaveRows : fa::kFwdWaveRows);
     p.nqt = (Sq + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;
@@ -191,7 +192,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
     if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
-    return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
+    return launch_status(wide ? fa::launch_fwd_wide(p, d, dtype == FA_BF16, false, stream)
+                              : fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
 }
 
 fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, float* lse, int B,
@@ -218,7 +220,7 @@ fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, f
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk;
     p.gw = fa::fwd_heads_per_wg(p.G);
-    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G, fa::kFwdWideWaveRows);
     p.nqt = (Sq + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;
@@ -235,7 +237,7 @@ fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, f
     }
     if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
-    return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
+    return launch_status(fa::launch_fwd_wide(p, d, dtype == FA_BF16, false, stream));
 }
 
 fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
@@ -260,8 +262,9 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out
     p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = max_seqlen_q; p.Sk = max_seqlen_k;
+    const bool wide = fa::fwd_use_wide(max_seqlen_k, causal, window_left, window_right);
     p.gw = fa::fwd_heads_per_wg(p.G);
-    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G, wide ? fa::kFwdWideWaveRows : fa::kFwdWaveRows);
     p.nqt = (max_seqlen_q + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;
@@ -272,7 +275,8 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out
     p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
     if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
-    return launch_status(fa::launch_fwd(p, d, dtype == FA_BF16, true, stream));
+    return launch_status(wide ? fa::launch_fwd_wide(p, d, dtype == FA_BF16, true, stream)
+                              : fa::launch_fwd(p, d, dtype == FA_BF16, true, stream));
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int max_seqlen_k, int d, int split_size) {
@@ -394,7 +398,7 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, f
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk; p.sk_pad = (Sk + 63) / 64 * 64;
     p.gw = fa::fwd_heads_per_wg(p.G);
-    p.bm = fa::fwd_rows_per_wg(p.G);
+    p.bm = fa::fwd_rows_per_wg(p.G, fa::kFwdWideWaveRows);
     p.nqt = (Sq + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;

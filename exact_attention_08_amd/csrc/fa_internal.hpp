@@ -28,7 +28,7 @@ struct FwdParams {
     uint32_t qsign;             // 0x80008000 when scale < 0 (q negated exactly), else 0
     int xcd_groups;             // (B*Hkv)/8 when B*Hkv % 8 == 0, else 0 (no remap)
     int gw;                     // query heads per work-group (fwd_heads_per_wg(G))
-    int bm;                     // query rows per work-group (fwd_rows_per_wg(G))
+    int bm;                     // query rows per work-group (fwd_rows_per_wg)
     // score modifiers (padded forward only)
     int mod;                    // bit 0: ALiBi bias, bit 1: soft-capping
     const float* alibi;         // [Hq] slopes (bias -slope * |pos - j|, natural-log units)
@@ -113,6 +113,7 @@ struct BwdParams {
 
 // Host launchers (defined next to their kernels).
 hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStream_t s);
+hipError_t launch_fwd_wide(const FwdParams& p, int d, bool bf16, bool varlen, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int d, bool bf16, hipStream_t s);
 
@@ -124,14 +125,30 @@ constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
 hipError_t decode_scratch(void** ptr);
 
 // Kernel tile geometry, shared with the host for grid sizing.
-constexpr int kFwdWaveRows = 64;   // query rows per forward wave
-constexpr int kFwdWaves = 4;       // waves per forward work-group (one per SIMD)
+constexpr int kFwdWaveRows = 32;      // query rows per wave of the 16-bit forward kernel
+constexpr int kFwdWideWaveRows = 64;  // rows per wave (two 32-row halves) of the score-modifier
+                                      // and 8-bit forward kernels
+constexpr int kFwdWaves = 4;          // waves per forward work-group (one per SIMD)
 constexpr int kFwdThreads = 64 * kFwdWaves;
 // A forward work-group covers gw query heads that share one K/V head (the
-// largest of 4, 2, 1 dividing G) and 64 * 4 / gw query rows, so its waves
-// need the same K/V tiles at the same steps.
+// largest of 4, 2, 1 dividing G) and wave_rows * 4 / gw query rows, so its
+// waves need the same K/V tiles at the same steps.
 inline int fwd_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
-inline int fwd_rows_per_wg(int G) { return kFwdWaveRows * kFwdWaves / fwd_heads_per_wg(G); }
+inline int fwd_rows_per_wg(int G, int wave_rows) { return wave_rows * kFwdWaves / fwd_heads_per_wg(G); }
+// The forward runs on one of two kernels, chosen by how many keys a query
+// row sees at most: the paired kernel (32-row waves, two work-groups per CU)
+// up to kFwdWideMinKeys, the wide kernel (64-row waves) beyond.  sk is the
+// key count (packed: its host bound); a left window bounds it by
+// window_left + 1 (+ window_right without causal).
+constexpr int kFwdWideMinKeys = 2048;
+inline bool fwd_use_wide(int sk, int causal, int wl, int wr) {
+    long long kpr = sk;
+    if (wl >= 0 && (causal || wr >= 0)) {
+        const long long band = (long long)wl + 1 + (causal ? 0 : wr);
+        kpr = kpr < band ? kpr : band;
+    }
+    return kpr > kFwdWideMinKeys;
+}
 constexpr int kDecodeWaves = 4;    // waves per decode split work-group
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr float kLog2e_host = 1.4426950408889634f;

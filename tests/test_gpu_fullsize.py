@@ -12,8 +12,8 @@ the benchmark times, against the fp64 oracle:
 Each check prints max |dO|, max |dLSE|, the count of elements above 1e-2
 (accepted only within one output ulp of an exact value of magnitude >= 2,
 see oracle/checks.py), the rounding floor of the output format and the
-largest distance of a GPU value from the correctly rounded exact value.  Properties that hold at any size are checked on the whole output as
-well (finite values; each output row lies inside the range of its K/V
+largest distance of a GPU value from the correctly rounded exact value.
+Properties that hold at any size are checked on the whole output as well (finite values; each output row lies inside the range of its K/V
 head's values; LSE is at least the diagonal key's score)."""
 import numpy as np
 import pytest
@@ -66,12 +66,12 @@ def test_causal_window_full():
     _check_all_rows(synth.WORKLOADS["causal_window"])
 
 
-def test_causal_window_band_form_equals_generic_form():
-    """At the sliding-window workload's full shape the band form (every step
-    in the interleaved pipeline, masks applied at region starts) gives the
-    same O bits as the generic masked-step form (reached through the score
-    modifier entry with zero ALiBi slopes, which keeps the plain order of
-    maxima); LSE may differ in its last bits (another fp32 summation tree)."""
+def test_causal_window_paired_kernel_equals_wide_kernel():
+    """At the sliding-window workload's full shape the paired kernel (which
+    fa_fwd uses for windows) gives the same O bits as the wide kernel's
+    masked steps (reached through the score modifier entry with zero ALiBi
+    slopes, which keeps the plain order of maxima); LSE may differ in its
+    last bits (another fp32 summation tree)."""
     w = synth.WORKLOADS["causal_window"]
     _, (o, lse), (qd, kd, vd) = _run_padded(w)
     zero = torch.zeros(w.Hq, dtype=torch.float32, device=DEV)
@@ -79,7 +79,7 @@ def test_causal_window_band_form_equals_generic_form():
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
     rel = ((lse - lse2).abs() / lse2.abs().clamp_min(1.0)).max().item()
-    print(f"[parity] {w.name}: band vs generic form: O bitwise equal, max rel dLSE {rel:.3g}",
+    print(f"[parity] {w.name}: paired vs wide kernel: O bitwise equal, max rel dLSE {rel:.3g}",
           flush=True)
     assert rel <= 4 * 2.0 ** -23
 

@@ -59,15 +59,20 @@ def test_mod_matches_oracle(case):
     log(compare(o, lse, ro, rl, dt, name), name)
 
 
-def test_zero_slopes_give_plain_bits():
-    """ALiBi with all-zero slopes adds exact zeros: the plain forward's bits."""
+def test_zero_slopes_give_the_plain_result():
+    """ALiBi with all-zero slopes adds exact zeros.  The modifier kernel and
+    the plain forward are different kernels (their fp32 sums are added in
+    different orders), so their results agree to rounding: O within one
+    output ulp, LSE within a few fp32 ulps."""
     print("[case] fwd_mod zero slopes", flush=True)
     q, k, v = synth.gen_padded(609, 2, 8, 2, 300, 300, 128, "bf16")
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o1, l1 = fa.fwd(qd, kd, vd, causal=True)
     o2, l2 = fa.fwd_mod(qd, kd, vd, causal=True, alibi_slopes=torch.zeros(8, device=DEV))
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    d_o = (o1.float() - o2.float()).abs()
+    assert torch.all(d_o <= 2.0 ** -7 * torch.maximum(o1.float().abs(), o2.float().abs()) + 1e-6)
+    assert ((l1 - l2).abs() / l2.abs().clamp_min(1.0)).max().item() <= 8 * 2.0 ** -23
 
 
 def test_no_modifier_is_the_plain_forward():
@@ -84,16 +89,15 @@ def test_no_modifier_is_the_plain_forward():
     (2, 8, 2, 700, 700, 128, "bf16", True, (100, 0)),
     (1, 4, 4, 530, 610, 64, "fp16", False, (90, 40)),
 ], ids=["causal_gqa_d128", "two_sided_sq_lt_sk_d64"])
-def test_band_form_gives_the_plain_forms_bits(shape):
-    """A left window sends fa_fwd through the band form of the kernel (every
-    computed step in the interleaved pipeline); ALiBi with zero slopes runs
-    the modifier kernel, which uses the generic masked steps and, with zero
-    slopes, the plain arithmetic.  O must agree bit for bit (the same
-    weights and 16-bit sums in the same order); the fp32 row sums behind
-    LSE are added in a different tree order on masked steps, so LSE may
-    differ in its last bits."""
+def test_window_paired_kernel_gives_the_wide_kernels_bits(shape):
+    """A sliding window sends fa_fwd to the paired kernel (32-row waves, two
+    work-groups per CU); ALiBi with zero slopes runs the wide modifier kernel
+    (64-row waves), whose masked steps take the plain arithmetic in the same
+    order.  O must agree bit for bit (the same weights and 16-bit sums in the
+    same order); the fp32 row sums behind LSE are added in a different tree
+    order, so LSE may differ in its last bits."""
     B, Hq, Hkv, Sq, Sk, d, dt, causal, window = shape
-    print(f"[case] band form vs generic form {shape}", flush=True)
+    print(f"[case] paired vs wide kernel {shape}", flush=True)
     q, k, v = synth.gen_padded(620, B, Hq, Hkv, Sq, Sk, d, dt)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o1, l1 = fa.fwd(qd, kd, vd, causal=causal, window=window)
