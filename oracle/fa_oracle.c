@@ -40,9 +40,18 @@
  * rows, which does not change any row's arithmetic.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads used by the row loops below (n < 1 leaves the OpenMP default);
+ * returns the number now in effect.  For timing the oracle on one core. */
+int fa_oracle_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+}
 
 /* Is key j visible from query row i?  Sequence lengths sq (queries) and sk
  * (keys); causal / window flags as described above. */

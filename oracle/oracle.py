@@ -59,7 +59,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                            i32, i32, i32, i32, i32, i32, f64]
     lib.fa_oracle_fwd_mod.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32,
                                       i32, i32, i32, f64, f64, P]
-    for f in (lib.fa_oracle_rows, lib.fa_oracle_fwd, lib.fa_oracle_varlen,
+    lib.fa_oracle_set_threads.argtypes = [i32]
+    for f in (lib.fa_oracle_set_threads, lib.fa_oracle_rows, lib.fa_oracle_fwd, lib.fa_oracle_varlen,
               lib.fa_oracle_decode, lib.fa_oracle_bwd, lib.fa_oracle_decode_paged,
               lib.fa_oracle_fwd_mod):
         f.restype = ctypes.c_int
@@ -137,6 +138,10 @@ class Oracle:
 
     def __init__(self, lib: ctypes.CDLL | None = None):
         self.lib = lib if lib is not None else load()
+
+    def set_threads(self, n: int) -> int:
+        """OpenMP threads of the row loops (n < 1: unchanged); returns the count in effect."""
+        return int(self.lib.fa_oracle_set_threads(int(n)))
 
     # -- padded batch ------------------------------------------------------
     def attention(self, q, k, v, causal=False, window=(-1, -1), scale=None):
