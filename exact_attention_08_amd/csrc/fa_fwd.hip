@@ -12,13 +12,13 @@
 // 32 query rows of one query head.  The waves of a work-group cover gw query
 // heads that read the same K/V head (gw = 4, 2 or 1, the largest dividing
 // G) and 128/gw rows, so they walk the same K/V tiles with the same masks in
-// lockstep.  Two work-groups share a CU (256 registers per wave, 64 KB of
-// LDS each at d = 128): the two waves on each SIMD belong to different
+// lockstep.  Three work-groups share a CU (at most 168 registers per wave,
+// 48 KB of LDS each at d = 128): the waves on each SIMD belong to different
 // work-groups and never synchronise with each other, so while one is in its
-// softmax the other's matrix instructions keep the MFMA pipe busy, and one
-// work-group's prologue and epilogue overlap the other's key loop.  (One
+// softmax the others' matrix instructions keep the MFMA pipe busy, and one
+// work-group's prologue and epilogue overlap the others' key loops.  (One
 // wave per SIMD has to interleave matrix and vector work within a single
-// instruction stream and stalls wherever that stream waits; two waves of one
+// instruction stream and stalls wherever that stream waits; waves of one
 // work-group fall into lockstep at every barrier.)
 //
 // Orientation.  Scores are computed transposed, S^T = K Q^T, with
@@ -42,9 +42,9 @@
 //     read a 4-key x 16-column block and each lane receives one column), so
 //     each V^T operand half is one contiguous 512-byte wave read.
 // Contiguous wave reads are bank-conflict free.  K and V are buffered in a
-// ring of 4 tiles; step r copies tile r+3 (its copies shared by the four
+// ring of 3 tiles; step r copies tile r+2 (its copies shared by the four
 // waves) and ends with one barrier that both publishes tile r+1 and frees
-// the slot tile r+4 will use.
+// the slot tile r+3 will use.
 //
 // Online softmax in base 2: scores are scaled by c = |scale|*log2(e) inside
 // one FMA feeding v_exp_f32.  A row's running max is raised only when its
@@ -70,8 +70,9 @@ struct FwdGeo {
     static constexpr int KK = BN / 16;          // reduction steps over keys
     static constexpr int TE = BN * D;           // elements of one K (or V) tile
     static constexpr int TB = TE * 2 / 1024;    // 1 KB blocks per K (or V) tile
-    static constexpr int STAGES = 5;            // LDS ring depth
-    static constexpr int AHEAD = 4;             // step r copies tile r + AHEAD
+    static constexpr int STAGES = 3;            // LDS ring depth
+    static constexpr int AHEAD = 2;             // step r copies tile r + AHEAD (into the
+                                                // slot that tile r - 1 used)
     static constexpr int LPS = 2 * TB / NW;     // DMA loads per wave per step
     static_assert((2 * TB) % NW == 0, "the blocks of a tile pair split evenly over the waves");
     static_assert(AHEAD + 1 == STAGES, "a slot is refilled right after the barrier that retires it");
@@ -90,12 +91,14 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
 }
 
 template <int D, bool BF16, bool VARLEN>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fa_fwd_kernel(FwdParams p) {
     using T = FwdGeo<D>;
     constexpr int TE = T::TE;
-    __shared__ __attribute__((aligned(1024))) uint16_t k_ring[T::STAGES * TE];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_ring[T::STAGES * TE];
+    // K slots 0 .. STAGES-1, then V slots; after the key loop the first
+    // 32 x D rows per wave stage the output
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * T::STAGES * TE];
+    static_assert(T::NW * T::R * D <= 2 * T::STAGES * TE, "output staging fits in the ring");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -221,8 +224,8 @@ void fa_fwd_kernel(FwdParams p) {
     };
     // ring slot i of K and of V (tile jt sits in slot (jt - tile_lo) % STAGES;
     // the steps carry that slot number instead of dividing)
-    auto kslot = [&](int i) __attribute__((always_inline)) { return k_ring + i * TE; };
-    auto vslot = [&](int i) __attribute__((always_inline)) { return v_ring + i * TE; };
+    auto kslot = [&](int i) __attribute__((always_inline)) { return ring + i * TE; };
+    auto vslot = [&](int i) __attribute__((always_inline)) { return ring + (T::STAGES + i) * TE; };
     auto next_slot = [&](int i) __attribute__((always_inline)) {
         return i == T::STAGES - 1 ? 0 : i + 1;
     };
@@ -236,17 +239,15 @@ void fa_fwd_kernel(FwdParams p) {
             else dma16_to_lds(vrs, vdst + dma_loff[l], dma_voff[l], 0);
         }
     };
-    // Step jt reads V of tile jt and K of tile jt + 1 (the scores of the next
-    // tile are computed beside this tile's softmax).  End of step jt: this
-    // wave's copies of every tile up to jt + 2 have landed (tiles jt + 3 and
-    // jt + 4 may still be in flight), its LDS reads have returned, then the
-    // barrier makes both true for all waves: tile jt + 2 is published and
-    // the slot of tile jt, which step jt + 1 refills with tile jt + 5, is
-    // free.  The wait and the barrier form one asm statement so that no LDS
-    // access is moved across them.
+    // End of step jt: this wave's copies of every tile up to jt + 1 have
+    // landed (tile jt + 2 may still be in flight), its LDS reads have
+    // returned, then the barrier makes both true for all waves: tile jt + 1
+    // is published and the slot of tile jt, which step jt + 1 refills with
+    // tile jt + 3, is free.  The wait and the barrier form one asm statement
+    // so that no LDS access is moved across them.
     auto sync_step = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
-                     ::"n"(T::LPS * (T::AHEAD - 2)) : "memory");
+                     ::"n"(T::LPS * (T::AHEAD - 1)) : "memory");
     };
 
     // ---- the wave's 32 query rows as MFMA B operands ----------------------
@@ -377,57 +378,34 @@ void fa_fwd_kernel(FwdParams p) {
         return acc;
     };
 
-    // Step jt (tile jt in slot i): operand loads of K(jt + 1) and V(jt)
-    // first, so that their latency passes under the softmax; then, for the
-    // tiles of this wave, the mask (boundary tiles only) and the softmax of
-    // tile jt; then the MFMAs of S(jt + 1) = K Q^T (every step, so that no
-    // step depends on which tiles this wave computes; past the last tile
-    // they read a published zero or stale slot and are discarded) one for
-    // one with those of O += V(jt) P(jt): no two neighbours depend on each
-    // other.  Two steps per iteration swap the roles of the two score
-    // accumulators.
-    auto step = [&](f32x16& cur, f32x16& nxt, int jt, int i) __attribute__((always_inline)) {
-        const int i1 = next_slot(i);
+    // Step jt (tile jt in ring slot i): this wave's copies of tile jt + 2,
+    // then, for the tiles of this wave, S^T = K Q^T, the mask (boundary
+    // tiles only), the softmax and O^T += V^T P^T; steps outside [w_lo,
+    // w_hi] only copy and synchronise.
+    auto step = [&](int jt, int i) __attribute__((always_inline)) {
         issue(jt + T::AHEAD, i == 0 ? T::STAGES - 1 : i - 1);
-        const bool comp = jt >= w_lo && jt <= w_hi;   // uniform per wave
-        u32x4 kq[T::KS], vq[T::KK][T::DB];
-        load_k(kq, i1);
-        if (comp) load_v(vq, i);
-        __builtin_amdgcn_sched_barrier(0);
-        if (comp) {
+        if (jt >= w_lo && jt <= w_hi) {                // uniform per wave
+            f32x16 cur = qk(i);
             if (jt < in_lo || jt > in_hi)
                 mask_acc32(cur, rel_lo - jt * T::BN, rel_hi - jt * T::BN);
             softmax_tile(cur);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+            u32x4 vq[T::KK][T::DB];
+            load_v(vq, i);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) nxt[e] = 0.f;
-        if (comp) {
+            for (int kk = 0; kk < T::KK; ++kk)
 #pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks) {
-                static_assert(T::KK * T::DB == T::KS, "one P.V MFMA beside each score MFMA");
-                nxt = mfma32x32x16<BF16>(kq[ks], qreg[ks], nxt);
-                const int kk = ks / T::DB, db = ks % T::DB;
-                oacc[db] = mfma32x32x16<BF16>(vq[kk][db], pb[kk], oacc[db]);
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < T::KS; ++ks) nxt = mfma32x32x16<BF16>(kq[ks], qreg[ks], nxt);
+                for (int db = 0; db < T::DB; ++db)
+                    oacc[db] = mfma32x32x16<BF16>(vq[kk][db], pb[kk], oacc[db]);
         }
         sync_step();
-        return i1;
+        return next_slot(i);
     };
     if (ntiles > 0) {
-        // tiles 0 .. AHEAD-1 in flight; the first step needs tiles 0 and 1
+        // tiles 0 .. AHEAD-1 in flight; the first step needs tile 0
         for (int s = 0; s < T::AHEAD; ++s) issue(tile_lo + s, s);
         sync_step();
-        f32x16 sa = qk(0), sb;
-        int jt = tile_lo, i = 0;
-        for (; jt + 1 <= tile_last; jt += 2) {
-            i = step(sa, sb, jt, i);
-            i = step(sb, sa, jt + 1, i);
-        }
-        if (jt <= tile_last) step(sa, sb, jt, i);
+        int i = 0;
+        for (int jt = tile_lo; jt <= tile_last; ++jt) i = step(jt, i);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // DMA loads of unused tiles still in flight
 
@@ -435,11 +413,11 @@ void fa_fwd_kernel(FwdParams p) {
     // O goes through LDS so that every store writes whole rows: in the
     // accumulator layout a store instruction would cover 16 bytes of each of
     // 32 rows.  Each wave stages its 32 x D tile in its own part of the
-    // (now idle) K ring, rows of D/8 16-byte chunks with chunk c of row r at
+    // (now idle) ring, rows of D/8 16-byte chunks with chunk c of row r at
     // c ^ (r % (D/8)) (conflict-free reads), then stores D/8 lanes per row.
     constexpr int CH = D / 8;                  // 16-byte chunks per row
     asm volatile("s_barrier" ::: "memory");    // every wave is done with the ring
-    char* stage = reinterpret_cast<char*>(k_ring) + wave * (T::R * D * 2);
+    char* stage = reinterpret_cast<char*>(ring) + wave * (T::R * D * 2);
     const float l_tot = sum_halves(l_run);
     const float lr_tot = sum_halves(lr_run);
     const float inv = lr_tot > 0.f ? 1.f / lr_tot : 0.f;
