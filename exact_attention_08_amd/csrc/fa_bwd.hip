@@ -149,6 +149,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int SE = 4 * TE + 256;             // stage size in 16-bit elements
     constexpr int NS = kDkdvStages;
     __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * SE];
+    debug_poison_lds(ring, (int)sizeof(ring));
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -236,7 +237,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     // visible and every wave is done with step s-1, whose stage step s+NS-1
     // refills
     auto sync_step = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS * (NS - 2)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(FA_VMCNT(LPS * (NS - 2))) : "memory");
     };
 
     f32x16 dkt[T::DB], dvt[T::DB];               // dK^T, dV^T: lane = key, element = d
@@ -347,6 +348,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
     // stage s: K (A order), V (A order), K (T order)
     constexpr int NS = kDqStages;
     __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * 3 * TE];
+    debug_poison_lds(ring, (int)sizeof(ring));
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -465,7 +467,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         }
     };
     auto sync_step = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPS * (NS - 2)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(FA_VMCNT(LPS * (NS - 2))) : "memory");
     };
 
     f32x16 dqt[T::DB];                                    // dQ^T: lane = row, element = d

@@ -318,9 +318,9 @@ void fa_decode_split_kernel(DecodeParams p) {
         const int s = t & 1;
         load_v(next, jb + STEP);
         if (t + 1 < nb)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NVI + NKI) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FA_VMCNT(2 * NVI + NKI)) : "memory");
         else
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NVI) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(FA_VMCNT(2 * NVI)) : "memory");
         process(s, cur, jb);
         if (t + 2 < nb) {
             // the slot's K reads were consumed by the MFMAs above

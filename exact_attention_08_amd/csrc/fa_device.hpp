@@ -21,6 +21,36 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Checking build (FA_DEBUG_SYNC, the library libfa355_debug.so): every wait
+// of a copy pipeline drains all outstanding copies (FA_VMCNT(n) is 0), and
+// the forward and backward kernels fill their LDS rings with NaN before the
+// first copy, so that a tile read before its copy has landed, or a read of
+// bytes no copy writes, shows up as NaN in the results.  (The decode split
+// kernel, whose K slots are private to each wave, only drains.)  Its results
+// must equal the pipelined build's bit for bit.
+#ifdef FA_DEBUG_SYNC
+#define FA_VMCNT(n) 0
+constexpr bool kDebugSync = true;
+#else
+#define FA_VMCNT(n) (n)
+constexpr bool kDebugSync = false;
+#endif
+
+// (checking build only) all-ones words over [p, p + bytes): NaN as bf16,
+// fp16, e4m3 and fp32; then a barrier
+__device__ __forceinline__ void debug_poison_lds(void* p, int bytes) {
+    if constexpr (kDebugSync) {
+        // (an LDS pointer: stores through a generic one could alias the
+        // kernel arguments, which would then no longer be known uniform)
+        __attribute__((address_space(3))) uint32_t* w =
+            (__attribute__((address_space(3))) uint32_t*)(p);
+        const int n = bytes / 4;
+        for (int i = 0; i < n; i += blockDim.x)   // (a uniform trip count)
+            if (i + (int)threadIdx.x < n) w[i + threadIdx.x] = 0xffffffffu;
+        __syncthreads();
+    }
+}
+
 // One v_mfma_f32_32x32x16_{bf16,f16}: C[32x32] += A[32x16] * B[16x32].
 // Operand registers: lane l holds row (A) / column (B) l%32 and the 8
 // reduction slots of half l/32.  Result: lane l holds column l%32, element

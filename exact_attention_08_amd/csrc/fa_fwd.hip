@@ -99,6 +99,7 @@ void fa_fwd_kernel(FwdParams p) {
     // 32 x D rows per wave stage the output
     __shared__ __attribute__((aligned(1024))) uint16_t ring[2 * T::STAGES * TE];
     static_assert(T::NW * T::R * D <= 2 * T::STAGES * TE, "output staging fits in the ring");
+    debug_poison_lds(ring, (int)sizeof(ring));
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,7 +248,7 @@ void fa_fwd_kernel(FwdParams p) {
     // so that no LDS access is moved across them.
     auto sync_step = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
-                     ::"n"(T::LPS * (T::AHEAD - 1)) : "memory");
+                     ::"n"(FA_VMCNT(T::LPS * (T::AHEAD - 1))) : "memory");
     };
 
     // ---- the wave's 32 query rows as MFMA B operands ----------------------

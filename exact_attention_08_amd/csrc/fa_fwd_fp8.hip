@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(1, 
 void fa_fwd_fp8_kernel(Fp8Params p) {
     using T = Fp8Geo<D>;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[T::STAGES * T::TILE];
+    debug_poison_lds(ring, (int)sizeof(ring));
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -261,7 +262,7 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
     // landed (those of jt + 2 .. jt + STAGES - 3 may fly); the barrier then
     // makes every wave's copies visible and frees the slot of jt - 2.
     auto sync_step = [&]() __attribute__((always_inline)) {
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(T::LPS * (T::STAGES - 4)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(FA_VMCNT(T::LPS * (T::STAGES - 4))) : "memory");
     };
 
     auto ld_op = [&](const uint8_t* base) __attribute__((always_inline)) {
@@ -486,7 +487,7 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
     if (ntiles > 0) {
         // tiles tile_lo .. +STAGES-3 in flight; the first step needs the
         // first two landed (K of the first now, K of the second at its end)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(T::LPS * (T::STAGES - 4)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(FA_VMCNT(T::LPS * (T::STAGES - 4))) : "memory");
         {
             const uint8_t* tl = slot(tile_lo);
 #pragma unroll

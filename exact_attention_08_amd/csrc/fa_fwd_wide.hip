@@ -138,6 +138,8 @@ void fa_fwd_wide_kernel(FwdParams p) {
     constexpr int TE = T::TILE_ELEMS;
     __shared__ __attribute__((aligned(1024))) uint16_t k_ring[T::STAGES * TE];
     __shared__ __attribute__((aligned(1024))) uint16_t v_ring[T::STAGES * TE];
+    debug_poison_lds(k_ring, (int)sizeof(k_ring));
+    debug_poison_lds(v_ring, (int)sizeof(v_ring));
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -311,7 +313,7 @@ void fa_fwd_wide_kernel(FwdParams p) {
     // statement so that no LDS access is moved across them.
     auto sync_pair = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
-                     ::"n"(T::LPS * (T::STAGES - 5)) : "memory");
+                     ::"n"(FA_VMCNT(T::LPS * (T::STAGES - 5))) : "memory");
     };
 
     // ---- the wave's 2 x 32 query rows as MFMA B operands ------------------

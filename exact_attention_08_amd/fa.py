@@ -7,6 +7,7 @@ fallback: if the library is missing or a call fails, a RuntimeError says so.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -16,6 +17,10 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa355.so")
+# The checking build of the same sources (every copy-pipeline wait drained,
+# LDS rings filled with NaN before first use): for tests that compare it with
+# the pipelined library bit for bit.
+DEBUG_LIB_PATH = os.path.join(_PKG, "libfa355_debug.so")
 
 FA_BF16, FA_FP16 = 0, 1
 _DTYPE = {torch.bfloat16: FA_BF16, torch.float16: FA_FP16}
@@ -28,7 +33,8 @@ EXPORTS = ("fa_fwd", "fa_fwd_mod", "fa_fwd_fp8_workspace_bytes", "fa_fwd_fp8", "
            "fa_last_error")
 
 _lock = threading.Lock()
-_lib = None
+_libs: dict = {}
+_active = threading.local()     # path of the library calls go to (default LIB_PATH)
 
 
 class FAError(RuntimeError):
@@ -39,12 +45,14 @@ class FAError(RuntimeError):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load the built library and declare its C signatures."""
-    global _lib
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load a built library (default: the one calls currently go to) and
+    declare its C signatures."""
+    if path is None:
+        path = getattr(_active, "path", None) or LIB_PATH
     with _lock:
-        if _lib is not None:
-            return _lib
+        if path in _libs:
+            return _libs[path]
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{path} is missing: the HIP library is not built "
@@ -82,8 +90,20 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_last_error.argtypes = []
         lib.fa_last_error.restype = ctypes.c_char_p
-        _lib = lib
+        _libs[path] = lib
         return lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route this thread's calls to the library at path (e.g. DEBUG_LIB_PATH)
+    inside the block."""
+    old = getattr(_active, "path", None)
+    _active.path = path
+    try:
+        yield load(path)
+    finally:
+        _active.path = old
 
 
 def _check(status: int) -> None:

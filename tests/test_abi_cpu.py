@@ -274,10 +274,21 @@ def test_status_strings(lib):
 
 def test_binding_fails_loudly_without_library(tmp_path):
     from exact_attention_08_amd import fa
-    saved = fa._lib
-    fa._lib = None
-    try:
-        with pytest.raises(RuntimeError, match="not built"):
-            fa.load(str(tmp_path / "missing.so"))
-    finally:
-        fa._lib = saved
+    with pytest.raises(RuntimeError, match="not built"):
+        fa.load(str(tmp_path / "missing.so"))
+    # calls routed to a missing library raise too (no fallback)
+    with pytest.raises(RuntimeError, match="not built"):
+        with fa.using(str(tmp_path / "missing.so")):
+            pass
+
+
+def test_checking_library_exports_the_same_symbols(lib):
+    """The checking build (libfa355_debug.so) exports every declared entry
+    point, like the pipelined library."""
+    from exact_attention_08_amd import fa
+    assert os.path.exists(fa.DEBUG_LIB_PATH)
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.DEBUG_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
