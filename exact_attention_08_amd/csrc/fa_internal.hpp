@@ -1,5 +1,6 @@
 // fa_internal.hpp -- parameter blocks shared by the host launcher (fa_api.cpp)
-// and the kernels (fa_fwd.hip, fa_fwd_fp8.hip, fa_decode.hip, fa_bwd.hip).
+// and the kernels (fa_fwd.hip, fa_fwd_wide.hip, fa_fwd_fp8.hip, fa_decode.hip,
+// fa_bwd.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -126,8 +127,8 @@ hipError_t decode_scratch(void** ptr);
 
 // Kernel tile geometry, shared with the host for grid sizing.
 constexpr int kFwdWaveRows = 32;      // query rows per wave of the 16-bit forward kernel
-constexpr int kFwdWideWaveRows = 64;  // rows per wave (two 32-row halves) of the score-modifier
-                                      // and 8-bit forward kernels
+constexpr int kFwdWideWaveRows = 64;  // rows per wave (two 32-row halves) of the wide 16-bit
+                                      // kernel and of the 8-bit kernel
 constexpr int kFwdWaves = 4;          // waves per forward work-group (one per SIMD)
 constexpr int kFwdThreads = 64 * kFwdWaves;
 // A forward work-group covers gw query heads that share one K/V head (the
@@ -135,9 +136,10 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 // waves need the same K/V tiles at the same steps.
 inline int fwd_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 inline int fwd_rows_per_wg(int G, int wave_rows) { return wave_rows * kFwdWaves / fwd_heads_per_wg(G); }
-// The forward runs on one of two kernels, chosen by how many keys a query
-// row sees at most: the paired kernel (32-row waves, two work-groups per CU)
-// up to kFwdWideMinKeys, the wide kernel (64-row waves) beyond.  sk is the
+// The 16-bit forward runs on one of two kernels, chosen by how many keys a
+// query row sees at most: the paired kernel (32-row waves, three work-groups
+// per CU) up to kFwdWideMinKeys, the wide kernel (64-row waves) beyond and
+// for every call with score modifiers.  sk is the
 // key count (packed: its host bound); a left window bounds it by
 // window_left + 1 (+ window_right without causal).
 constexpr int kFwdWideMinKeys = 2048;

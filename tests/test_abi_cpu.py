@@ -19,6 +19,8 @@ MISALIGNED = 0x10002
 @pytest.fixture(scope="module")
 def lib():
     from exact_attention_08_amd import fa
+    if os.environ.get("FA_TEST_LIB"):       # a host build (the sanitizer run)
+        return fa.load(os.environ["FA_TEST_LIB"])
     if not os.path.exists(fa.LIB_PATH):
         from exact_attention_08_amd import build_ext
         build_ext.build()
@@ -292,3 +294,12 @@ def test_checking_library_exports_the_same_symbols(lib):
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
     for name in declared_functions():
         assert name in exported, name
+
+
+def test_package_exports_a_binding_for_every_entry_point():
+    import exact_attention_08_amd as pkg
+    for name in declared_functions():
+        if name in ("fa_status_str", "fa_last_error"):
+            continue                      # surfaced through FAError
+        py = name[len("fa_"):]
+        assert py in pkg.__all__ and callable(getattr(pkg, py)), py
