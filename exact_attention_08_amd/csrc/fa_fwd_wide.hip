@@ -157,11 +157,27 @@ void fa_fwd_wide_kernel(FwdParams p) {
         const int i = blockIdx.x;
         if (p.xcd_groups > 0) {
             // Keep the head groups of one K/V head (and its neighbouring
-            // query tiles) on one XCD: work-group i runs on XCD i % 8.
+            // query tiles) on one XCD: work-group i runs on XCD i % 8.  A
+            // padded batch interleaves the XCD's (sequence, K/V head) groups
+            // tile by tile; packed sequences take one group after another,
+            // so the work-groups in flight on an XCD share one group's K/V
+            // in its L2 (16 packed sequences of 2 K-8 K tokens: 4.1 ms
+            // interleaved, 3.3 ms group after group).
             const int xcd = i & 7, r = i >> 3;
-            const int per_row = p.xcd_groups * gpk;
-            const int trev = r / per_row, rem = r - trev * per_row;
-            const int jgrp = rem / gpk, gq = rem - jgrp * gpk;
+            int trev, jgrp, gq;
+            if constexpr (VARLEN) {
+                const int per_grp = p.nqt * gpk;
+                jgrp = r / per_grp;
+                const int rem = r - jgrp * per_grp;
+                trev = rem / gpk;
+                gq = rem - trev * gpk;
+            } else {
+                const int per_row = p.xcd_groups * gpk;
+                trev = r / per_row;
+                const int rem = r - trev * per_row;
+                jgrp = rem / gpk;
+                gq = rem - jgrp * gpk;
+            }
             const int grp = xcd + 8 * jgrp;
             b = grp / p.Hkv;
             hg = (grp - b * p.Hkv) * gpk + gq;
