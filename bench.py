@@ -123,16 +123,19 @@ def _round_stats(st):
     return {k: round(v, 5) for k, v in st.items()}
 
 
-def fwd_kernel(sk: int, causal: bool, window) -> tuple[str, str]:
-    """(kernel name, source file) that fa_fwd / fa_fwd_varlen launch for keys
-    per row up to sk: the rule of the host launcher (fwd_use_wide)."""
-    kpr = sk
+def fwd_kernel(sq: int, sk: int, causal: bool, window) -> tuple[str, str]:
+    """(kernel name, source file) that fa_fwd / fa_fwd_varlen launch for
+    sq rows and sk keys (packed: the host bounds): the rule of the host
+    launcher (fwd_use_wide: average keys per row above 2560 -> wide)."""
     wl, wr = window
-    if wl >= 0 and wl >= sk - 1:
+    if wl >= sk - 1:
         wl = -1
+    if wr >= sq - 1:
+        wr = -1
+    kpr = sk - (min(sq, sk) // 2 if causal else 0)
     if wl >= 0 and (causal or wr >= 0):
         kpr = min(kpr, wl + 1 + (0 if causal else wr))
-    if kpr > 2048:
+    if kpr > 2560:
         return "fa_fwd_wide_kernel", "fa_fwd_wide.hip"
     return "fa_fwd_kernel", "fa_fwd.hip"
 
@@ -175,7 +178,7 @@ def bench_fwd_padded(steps, warmup, w, inputs=None):
         fa.fwd(qd, kd, vd, causal=w.causal, window=w.window, out=out, lse=lse)
 
     wall, stats = _timed(step, steps, warmup)
-    kernel, src = fwd_kernel(w.Sk, w.causal, w.window)
+    kernel, src = fwd_kernel(w.Sq, w.Sk, w.causal, w.window)
     hbm = work["flop"] / work["bytes"] < metrics.PEAK_BF16_TFLOPS * 1e12 / (metrics.PEAK_HBM_GBS * 1e9)
     leg = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Sq": w.Sq, "Sk": w.Sk,
            "d": w.d, "dtype": w.dtype, "causal": w.causal, "window": list(w.window),
@@ -201,7 +204,7 @@ def bench_fwd_varlen(steps, warmup, w):
                       lse=lse)
 
     wall, stats = _timed(step, steps, warmup)
-    kernel, src = fwd_kernel(mx, w.causal, w.window)
+    kernel, src = fwd_kernel(mx, mx, w.causal, w.window)
     leg = {"workload": w.name, "sequences": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
            "dtype": w.dtype, "causal": w.causal, "total_tokens": int(cu[-1]), "max_len": mx,
            "algorithmic_flop": work["flop"], "algorithmic_bytes": work["bytes"],

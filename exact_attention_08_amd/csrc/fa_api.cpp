@@ -179,7 +179,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* out, float
     p.cu_q = nullptr; p.cu_k = nullptr;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk;
-    const bool wide = fa::fwd_use_wide(Sk, causal, window_left, window_right);
+    const bool wide = fa::fwd_use_wide(Sq, Sk, causal, window_left, window_right);
     p.gw = fa::fwd_heads_per_wg(p.G);
     p.bm = fa::fwd_rows_per_wg(p.G, wide ? fa::kFwdWideWaveRows : fa::kFwdWaveRows);
     p.nqt = (Sq + p.bm - 1) / p.bm;
@@ -262,7 +262,8 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out
     p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = max_seqlen_q; p.Sk = max_seqlen_k;
-    const bool wide = fa::fwd_use_wide(max_seqlen_k, causal, window_left, window_right);
+    const bool wide = fa::fwd_use_wide(max_seqlen_q, max_seqlen_k, causal, window_left,
+                                        window_right);
     p.gw = fa::fwd_heads_per_wg(p.G);
     p.bm = fa::fwd_rows_per_wg(p.G, wide ? fa::kFwdWideWaveRows : fa::kFwdWaveRows);
     p.nqt = (max_seqlen_q + p.bm - 1) / p.bm;

@@ -1,9 +1,10 @@
 // fa_fwd_wide.hip -- the wide fused exact-attention forward for gfx950:
 // 64 query rows per wave, one wave per SIMD.  Used where query rows see
-// many keys (more than kFwdWideMinKeys), where reading each K/V operand once
-// for 64 rows (half the LDS bytes per MFMA of 32-row waves) pays for having
-// one instruction stream per SIMD, and for the score modifiers (fa_fwd_mod).
-// Rows that see fewer keys go to fa_fwd.hip's paired kernel.
+// many keys (more than kFwdWideMinKeys on average), where reading each K/V
+// operand once for 64 rows (half the LDS bytes per MFMA of 32-row waves)
+// pays for having one instruction stream per SIMD, and for the score
+// modifiers (fa_fwd_mod).  Rows that see fewer keys go to fa_fwd.hip's
+// paired kernel.
 //
 // The method: the "FlashAttention" explainer page, steps 1-4 (tile the
 // sequence axis, score a tile on chip, online softmax with running max and

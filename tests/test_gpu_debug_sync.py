@@ -31,13 +31,14 @@ def _equal(a, b, name):
 
 
 # B, Hq, Hkv, Sq, Sk, d, dtype, causal, window: both forward kernels (rows that
-# see up to 2048 keys / more), ragged tails, windows, d = 64
+# see up to 2,560 keys on average / more), ragged tails, windows, d = 64
 FWD = [
     (2, 8, 2, 300, 300, 128, "bf16", True, (-1, -1)),
     (1, 4, 4, 700, 700, 128, "fp16", True, (100, 100)),
     (2, 4, 1, 130, 257, 64, "bf16", False, (-1, -1)),
     (1, 8, 2, 2200, 2200, 128, "bf16", True, (-1, -1)),
-    (1, 4, 2, 300, 2500, 64, "fp16", True, (-1, -1)),
+    (1, 8, 2, 5300, 5300, 128, "bf16", True, (-1, -1)),
+    (1, 4, 2, 300, 2900, 64, "fp16", True, (-1, -1)),
 ]
 
 
@@ -52,7 +53,7 @@ def test_forward_checking_build(case):
 
 def test_varlen_checking_build():
     print("[case] checking build varlen", flush=True)
-    lens = [1, 127, 300, 0, 2300, 64]
+    lens = [1, 127, 300, 0, 5400, 64]
     q, k, v, cu, _ = synth.gen_varlen(702, len(lens), 0, 0, 8, 2, 128, "bf16", lengths=lens)
     q, k, v, cu = q.to(DEV), k.to(DEV), v.to(DEV), cu.to(DEV)
     for mx in (300, max(lens)):           # the paired kernel, then the wide one

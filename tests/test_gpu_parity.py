@@ -45,17 +45,27 @@ FWD_CASES = [
     ("xcd_grouped_heads", 2, 16, 4, 256, 256, 128, "bf16", True, (-1, -1), None, 119),
     ("xcd_grouped_d64", 4, 8, 2, 200, 200, 64, "fp16", True, (-1, -1), None, 120),
     ("sigma_large_scores", 1, 4, 2, 256, 256, 128, "bf16", True, (-1, -1), 0.5, 121),
-    # rows that see more than 2048 keys run on the wide kernel (64-row
-    # waves): the same mask modes and edge cases on that side of the split
-    ("wide_causal_sq_lt_sk", 1, 4, 2, 300, 2500, 128, "bf16", True, (-1, -1), None, 131),
-    ("wide_noncausal_ragged", 1, 2, 1, 200, 2113, 128, "fp16", False, (-1, -1), None, 132),
-    ("wide_causal_gqa", 1, 8, 2, 2200, 2200, 128, "bf16", True, (-1, -1), None, 133),
-    ("wide_d64_fp16", 2, 4, 2, 150, 2090, 64, "fp16", True, (-1, -1), None, 134),
-    ("wide_window_left", 1, 4, 4, 2400, 2400, 128, "bf16", True, (2100, -1), None, 135),
-    ("wide_window_two_sided", 1, 2, 2, 100, 3000, 128, "bf16", False, (1500, 1000), None, 136),
-    ("wide_causal_sq_gt_sk", 1, 2, 2, 2300, 2100, 128, "bf16", True, (-1, -1), None, 137),
-    ("wide_negative_scale", 1, 2, 1, 64, 2049, 64, "bf16", False, (-1, -1), -0.07, 138),
-    ("wide_group3", 1, 6, 2, 128, 2300, 128, "bf16", True, (-1, -1), None, 139),
+    # rows of 2,000-3,000 keys on the paired kernel (32-row waves)
+    ("long_causal_sq_lt_sk", 1, 4, 2, 300, 2500, 128, "bf16", True, (-1, -1), None, 131),
+    ("long_noncausal_ragged", 1, 2, 1, 200, 2113, 128, "fp16", False, (-1, -1), None, 132),
+    ("long_causal_gqa", 1, 8, 2, 2200, 2200, 128, "bf16", True, (-1, -1), None, 133),
+    ("long_d64_fp16", 2, 4, 2, 150, 2090, 64, "fp16", True, (-1, -1), None, 134),
+    ("long_window_left", 1, 4, 4, 2400, 2400, 128, "bf16", True, (2100, -1), None, 135),
+    ("long_window_two_sided", 1, 2, 2, 100, 3000, 128, "bf16", False, (1500, 1000), None, 136),
+    ("long_causal_sq_gt_sk", 1, 2, 2, 2300, 2100, 128, "bf16", True, (-1, -1), None, 137),
+    ("long_negative_scale", 1, 2, 1, 64, 2049, 64, "bf16", False, (-1, -1), -0.07, 138),
+    ("long_group3", 1, 6, 2, 128, 2300, 128, "bf16", True, (-1, -1), None, 139),
+    # rows that see more than 2,560 keys on average run on the wide kernel
+    # (64-row waves): the same mask modes and edge cases on that side
+    ("wide_causal_sq_lt_sk", 1, 4, 2, 300, 3000, 128, "bf16", True, (-1, -1), None, 141),
+    ("wide_noncausal_ragged", 1, 2, 1, 200, 2613, 128, "fp16", False, (-1, -1), None, 142),
+    ("wide_causal_gqa", 1, 8, 2, 5200, 5200, 128, "bf16", True, (-1, -1), None, 143),
+    ("wide_d64_fp16", 2, 4, 2, 150, 2700, 64, "fp16", True, (-1, -1), None, 144),
+    ("wide_window_left", 1, 4, 4, 5400, 5400, 128, "bf16", True, (2600, -1), None, 145),
+    ("wide_window_two_sided", 1, 2, 2, 100, 3000, 128, "bf16", False, (1500, 1100), None, 146),
+    ("wide_causal_sq_gt_sk", 1, 2, 2, 6000, 5300, 128, "bf16", True, (-1, -1), None, 147),
+    ("wide_negative_scale", 1, 2, 1, 64, 2600, 64, "bf16", False, (-1, -1), -0.07, 148),
+    ("wide_group3", 1, 6, 2, 128, 2800, 128, "bf16", True, (-1, -1), None, 149),
 ]
 
 
@@ -80,9 +90,12 @@ VARLEN_CASES = [
     ("window_d64_fp16", [90, 257, 31], None, 4, 1, 64, "fp16", True, (32, 0), 203),
     ("many_short_xcd", [40, 7, 130, 66, 1, 99, 128, 255], None, 8, 1, 128, "bf16", True,
      (-1, -1), 204),
-    # a sequence longer than 2048 keys: the wide kernel's packed form
-    ("wide_packed", [2200, 30, 0, 700], None, 4, 2, 128, "bf16", True, (-1, -1), 205),
-    ("wide_packed_d64", [100, 2100], [2300, 2100], 2, 2, 64, "fp16", False, (-1, -1), 206),
+    # longer sequences: the paired kernel up to 2,560 keys per row on
+    # average, the wide kernel's packed form beyond
+    ("long_packed", [2200, 30, 0, 700], None, 4, 2, 128, "bf16", True, (-1, -1), 205),
+    ("long_packed_d64", [100, 2100], [2300, 2100], 2, 2, 64, "fp16", False, (-1, -1), 206),
+    ("wide_packed", [5400, 30, 0, 700], None, 4, 2, 128, "bf16", True, (-1, -1), 207),
+    ("wide_packed_d64", [100, 2100], [2700, 2100], 2, 2, 64, "fp16", False, (-1, -1), 208),
 ]
 
 

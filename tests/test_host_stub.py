@@ -48,18 +48,23 @@ def fwd(lib, B=1, Hq=8, Hkv=2, Sq=256, Sk=256, d=128, causal=1, wl=-1, wr=-1, sc
                       dtype, stream)
 
 
-# Sq, Sk, causal, wl, wr -> kernel: the paired kernel while a row sees at most
-# 2048 keys, the wide kernel beyond (a window bounds the keys per row)
+# Sq, Sk, causal, wl, wr -> kernel: the paired kernel while a row sees at
+# most 2560 keys on average (causal: Sk - min(Sq, Sk)/2; a left window bounds
+# a row by wl + 1 (+ wr without causal)), the wide kernel beyond
 DISPATCH = [
-    (2048, 2048, 1, -1, -1, "paired"),
-    (2049, 2049, 1, -1, -1, "wide"),
-    (64, 2049, 0, -1, -1, "wide"),
+    (4096, 4096, 1, -1, -1, "paired"),
+    (5120, 5120, 1, -1, -1, "paired"),         # 5120 - 2560 = 2560
+    (5122, 5122, 1, -1, -1, "wide"),           # 5122 - 2561 = 2561
+    (64, 2592, 1, -1, -1, "paired"),           # 2592 - 32
+    (64, 2594, 1, -1, -1, "wide"),
+    (8000, 2700, 1, -1, -1, "paired"),         # Sq > Sk: 2700 - 1350
+    (64, 2560, 0, -1, -1, "paired"),
+    (64, 2561, 0, -1, -1, "wide"),
     (4096, 8192, 1, 1000, -1, "paired"),
-    (4096, 8192, 1, 2047, -1, "paired"),
-    (4096, 8192, 1, 2048, -1, "wide"),
-    (4096, 8192, 0, 1000, 1000, "paired"),
-    (4096, 8192, 0, 1000, 1047, "paired"),
-    (4096, 8192, 0, 1000, 1048, "wide"),
+    (4096, 8192, 1, 2559, -1, "paired"),
+    (4096, 8192, 1, 2560, -1, "wide"),
+    (4096, 8192, 0, 1000, 1559, "paired"),
+    (4096, 8192, 0, 1000, 1560, "wide"),
     (4096, 8192, 0, 1000, -1, "wide"),        # no right bound: rows see up to 8192 keys
     (4096, 8192, 0, -1, 1000, "wide"),
 ]
@@ -88,7 +93,7 @@ def test_window_that_cuts_no_row_is_dropped(lib, stub):
 
 # Hq, Hkv -> heads per work-group gw; rows per work-group = wave rows x 4 / gw
 @pytest.mark.parametrize("Hq,Hkv,gw", [(8, 2, 4), (8, 8, 1), (12, 2, 2), (6, 2, 1), (32, 4, 4)])
-@pytest.mark.parametrize("Sk,wave_rows", [(1000, 32), (3000, 64)])
+@pytest.mark.parametrize("Sk,wave_rows", [(1000, 32), (4000, 64)])
 def test_forward_tiles_and_strides(lib, stub, Hq, Hkv, gw, Sk, wave_rows):
     B, Sq, d = 3, 1000, 64
     assert fwd(lib, B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Sk=Sk, d=d) == FA_OK
@@ -149,15 +154,16 @@ def test_fwd_mod_uses_the_wide_kernel(lib, stub):
     assert stub.kernel == "paired" and stub.fwd()["mod"] == 0
 
 
-@pytest.mark.parametrize("maxk,kernel", [(2048, "paired"), (2049, "wide")])
-def test_varlen_params(lib, stub, maxk, kernel):
-    st = lib.fa_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, OTHER, 5, 16, 4, 1500, maxk, 7000,
+@pytest.mark.parametrize("maxq,maxk,kernel", [(1500, 2048, "paired"), (5120, 5120, "paired"),
+                                               (5200, 5200, "wide")])
+def test_varlen_params(lib, stub, maxq, maxk, kernel):
+    st = lib.fa_fwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, OTHER, 5, 16, 4, maxq, maxk, 7000,
                            128, 1, -1, -1, 0.1, 0, None)
     assert st == FA_OK and stub.kernel == kernel
     p = stub.fwd()
     bm = (32 if kernel == "paired" else 64) * 4 // 4
     assert p["varlen"] == 1 and (p["cu_q"], p["cu_k"]) == (FAKE, OTHER)
-    assert (p["Sq"], p["Sk"], p["nqt"]) == (1500, maxk, -(-1500 // bm))
+    assert (p["Sq"], p["Sk"], p["nqt"]) == (maxq, maxk, -(-maxq // bm))
     assert (p["lse_b_stride"], p["lse_h_stride"]) == (0, 7000)
 
 
