@@ -398,8 +398,11 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, f
     p.q = q; p.k = k; p.v = v; p.vt = workspace; p.o = out; p.lse = lse;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk; p.sk_pad = (Sk + 63) / 64 * 64;
+    // the 16-bit forward's rule picks the paired (32-row waves) or the wide
+    // (64-row waves) form
+    const bool wide = fa::fwd_use_wide(Sq, Sk, causal, window_left, window_right);
     p.gw = fa::fwd_heads_per_wg(p.G);
-    p.bm = fa::fwd_rows_per_wg(p.G, fa::kFwdWideWaveRows);
+    p.bm = fa::fwd_rows_per_wg(p.G, wide ? fa::kFwdWideWaveRows : fa::kFwdWaveRows);
     p.nqt = (Sq + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;
@@ -413,7 +416,7 @@ fa_status_t fa_fwd_fp8(const void* q, const void* k, const void* v, void* out, f
     p.xcd_groups = ((long long)B * Hkv) % 8 == 0 ? (B * Hkv) / 8 : 0;
     if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
-    return launch_status(fa::launch_fwd_fp8(p, d, stream));
+    return launch_status(fa::launch_fwd_fp8(p, d, wide, stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq) {

@@ -548,18 +548,319 @@ void fa_fwd_fp8_kernel(Fp8Params p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Paired form of the 8-bit forward, for rows that see up to kFwdWideMinKeys
+// keys on average (the rule of the 16-bit forward): 32 query rows per wave
+// and three work-groups per CU, whose waves share each SIMD, as in the
+// 16-bit paired kernel.  One wave per SIMD (the kernel above) issues its
+// vector work from one instruction stream, and the weights' vector work
+// (scale, exponential, e4m3 packing, sum) outweighs the 8-bit MFMAs beside
+// it; three independent waves per SIMD issue it side by side.  Operand
+// layouts, copies, masks, lazy max and epilogue are those of the kernel
+// above; the ring has three stages of one 64-key tile (K, then V^T), copies
+// go out two tiles ahead, and a window's tiles are taken in the rotated
+// order of the 16-bit paired kernel.
 template <int D>
-static hipError_t launch_fp8_t(const Fp8Params& p, hipStream_t s) {
+struct Fp8PairGeo {
+    static constexpr int R = 32;                  // rows per wave
+    static constexpr int NW = kFwdWaves;          // waves per work-group
+    static constexpr int BN = 64;                 // keys per step (two 32-key sub-tiles)
+    static constexpr int KC = D / 64;             // reduction chunks of S over d
+    static constexpr int DB = D / 32;             // O^T accumulators
+    static constexpr int KBLK = 2 * KC * 2;       // 1 KB blocks of a K tile (sub-tile, kc, half)
+    static constexpr int VBLK = DB * 2;           // 1 KB blocks of a V^T tile (db, half)
+    static constexpr int TILE = (KBLK + VBLK) * 1024;
+    static constexpr int STAGES = 3;
+    static constexpr int AHEAD = 2;
+    static constexpr int LPS = (KBLK + VBLK) / NW;
+    static_assert((KBLK + VBLK) % NW == 0, "blocks split evenly over the waves");
+    static_assert(AHEAD == STAGES - 1, "a slot is refilled one step after its tile is used");
+};
+
+template <int D>
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void fa_fwd_fp8_paired_kernel(Fp8Params p) {
+    using T = Fp8PairGeo<D>;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[T::STAGES * T::TILE];
+    debug_poison_lds(ring, (int)sizeof(ring));
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int lq = lane & 31;
+    const int g = lane >> 5;
+    __builtin_assume(wave >= 0 && wave < T::NW);
+
+    // ---- work-group -> (query tile, head group, sequence), heaviest first
+    const int gw = p.gw, gpk = p.G / gw;
+    int t, hg, b;
+    {
+        const int i = blockIdx.x;
+        if (p.xcd_groups > 0) {
+            const int xcd = i & 7, r = i >> 3;
+            const int per_row = p.xcd_groups * gpk;
+            const int trev = r / per_row, rem = r - trev * per_row;
+            const int jgrp = rem / gpk, gq = rem - jgrp * gpk;
+            const int grp = xcd + 8 * jgrp;
+            b = grp / p.Hkv;
+            hg = (grp - b * p.Hkv) * gpk + gq;
+            t = p.nqt - 1 - trev;
+        } else {
+            const int ngrp = p.Hq / gw;
+            const int per_row = p.B * ngrp;
+            const int trev = i / per_row, rem = i - trev * per_row;
+            b = rem / ngrp;
+            hg = rem - b * ngrp;
+            t = p.nqt - 1 - trev;
+        }
+    }
+    const int hq = hg * gw + wave % gw;
+    const int hkv = hq / p.G;
+    const int sq = p.Sq, sk = p.Sk, delta = sk - sq;
+    const int q0 = t * p.bm;
+    if (q0 >= sq) return;                      // uniform over the work-group
+    const int causal = p.causal, wl = p.wl, wr = p.wr;
+    auto lo_of = [&](int i) __attribute__((always_inline)) { return wl >= 0 ? max(0, i + delta - wl) : 0; };
+    auto hi_of = [&](int i) __attribute__((always_inline)) {
+        int h = sk - 1;
+        if (causal) h = min(h, i + delta);
+        if (wr >= 0) h = min(h, i + delta + wr);
+        return h;
+    };
+
+    // ---- tile ranges (64-key tiles): the work-group walks [tile_lo,
+    // tile_last], this wave computes [w_lo, w_hi] and needs no mask on
+    // [in_lo, in_hi]
+    const int wg_last = min(q0 + p.bm, sq) - 1;
+    const int kv_lo = lo_of(q0), kv_hi = hi_of(wg_last);
+    const int tile_lo = kv_lo / T::BN;
+    const int ntiles = kv_hi >= kv_lo ? kv_hi / T::BN - tile_lo + 1 : 0;
+    const int tile_last = tile_lo + ntiles - 1;
+    const int r0 = q0 + T::R * (wave / gw);
+    int w_lo = 1, w_hi = 0;
+    if (r0 < sq) {
+        const int wlo = lo_of(r0), whi = hi_of(min(r0 + T::R - 1, sq - 1));
+        if (whi >= wlo) { w_lo = wlo / T::BN; w_hi = whi / T::BN; }
+    }
+    const int in_lo = (lo_of(min(r0 + T::R - 1, sq - 1)) + T::BN - 1) / T::BN;
+    const int int_hi = hi_of(r0);
+    const int in_hi = int_hi + 1 >= T::BN ? (int_hi + 1) / T::BN - 1 : -1;
+    // this lane's visible key interval, relative to its key offset 4g
+    int rel_lo, rel_hi;
+    {
+        const int pos = r0 + lq + delta;
+        rel_lo = (wl >= 0 ? pos - wl : -0x40000000) - 4 * g;
+        int hh = sk - 1;
+        if (causal) hh = min(hh, pos);
+        if (wr >= 0) hh = min(hh, pos + wr);
+        rel_hi = hh - 4 * g;
+    }
+
+    // ---- copies HBM/L2 -> LDS ring (block layout of the kernel above) -----
+    const int tok_q = (int)p.q_tok_stride, tok_kv = (int)p.kv_tok_stride;
+    const uint8_t* kseq = (const uint8_t*)p.k + ((long long)b * sk * p.Hkv + hkv) * D;
+    const uint8_t* vtrow = (const uint8_t*)p.vt + ((long long)b * p.Hkv + hkv) * D * p.sk_pad;
+    int dma_voff[T::LPS];
+    uint32_t dma_loff[T::LPS];
+    bool dma_isk[T::LPS];
+#pragma unroll
+    for (int i = 0; i < T::LPS; ++i) {
+        const int blk = wave + i * T::NW;
+        dma_isk[i] = blk < T::KBLK;
+        dma_loff[i] = blk * 1024;
+        if (dma_isk[i]) {
+            const int hh = blk & 1, kc = (blk >> 1) % T::KC, st = (blk >> 1) / T::KC;
+            dma_voff[i] = (32 * st + (lane & 31)) * tok_kv + 64 * kc + 32 * (lane >> 5) + 16 * hh;
+        } else {
+            const int vb = blk - T::KBLK, hh = vb & 1, db = vb >> 1;
+            dma_voff[i] = (32 * db + (lane & 31)) * p.sk_pad + 32 * (lane >> 5) + 16 * hh;
+        }
+    }
+    auto slot = [&](int i) __attribute__((always_inline)) { return ring + i * T::TILE; };
+    auto next_slot = [&](int i) __attribute__((always_inline)) {
+        return i == T::STAGES - 1 ? 0 : i + 1;
+    };
+    // this wave's copies of tile jt into ring slot i; tiles outside
+    // [tile_lo, tile_last] get zero records (zeros, no memory access)
+    auto issue = [&](int jt, int i) __attribute__((always_inline)) {
+        const bool valid = jt >= tile_lo && jt <= tile_last;
+        const int rows = valid ? min(sk - jt * T::BN, T::BN) : 0;
+        const i32x4 krs = scalar_rsrc(make_rsrc(kseq + (long long)(valid ? jt : 0) * T::BN * tok_kv,
+                                                rows * tok_kv));
+        const i32x4 vrs = scalar_rsrc(make_rsrc(vtrow + (long long)(valid ? jt : 0) * T::BN,
+                                                valid ? (D - 1) * p.sk_pad + T::BN : 0));
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(slot(i)));
+#pragma unroll
+        for (int l = 0; l < T::LPS; ++l)
+            dma16_to_lds(dma_isk[l] ? krs : vrs, dst + dma_loff[l], dma_voff[l], 0);
+    };
+    // End of step s: this wave's copies of the tiles of every step up to
+    // s + 1 have landed (step s + 2's may still be in flight), its LDS reads
+    // have returned; the barrier makes both true for all waves.
+    auto sync_step = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
+                     ::"n"(FA_VMCNT(T::LPS * (T::AHEAD - 1))) : "memory");
+    };
+    auto ld_op = [&](const uint8_t* base) __attribute__((always_inline)) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + lane * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + 1024 + lane * 16);
+        return (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+
+    // ---- the wave's 32 query rows as B operands ---------------------------
+    i32x8 qop[T::KC];
+    {
+        const auto qrs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const uint8_t*)p.q + ((long long)b * sq * p.Hq + hq) * D), (short)0, sq * tok_q,
+            0x00020000);
+#pragma unroll
+        for (int kc = 0; kc < T::KC; ++kc) {
+            const int off = (r0 + lq) * tok_q + 64 * kc + 32 * g;
+            const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0) ^ p.qsign;
+            const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0) ^ p.qsign;
+            qop[kc] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+    }
+
+    f32x16 oacc[T::DB];
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c = p.c;
+    i32x8 pb;
+
+    // weights of a tile (lazy max as in the kernel above): packs P, returns
+    // this lane's fp32 sum
+    auto exps = [&](const f32x16 (&sacc)[2], float m_use) __attribute__((always_inline)) {
+        float x[2][16];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[st][e] = exp2_fast(fmaf(sacc[st][e], c, -m_use));
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+            const int st = w >> 2, e = 4 * (w & 3);
+            pb[w] = (int)pack4_fp8(x[st][e], x[st][e + 1], x[st][e + 2], x[st][e + 3]);
+        }
+        float s4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            s4[j] = (x[0][4 * j] + x[0][4 * j + 1]) + (x[0][4 * j + 2] + x[0][4 * j + 3]) +
+                    ((x[1][4 * j] + x[1][4 * j + 1]) + (x[1][4 * j + 2] + x[1][4 * j + 3]));
+        return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    };
+    auto softmax_tile = [&](const f32x16 (&sacc)[2]) __attribute__((always_inline)) {
+        const bool first = m_run == -INFINITY;
+        float sum = exps(sacc, first ? 0.f : m_run);
+        if ((__builtin_amdgcn_ballot_w64(first) | __builtin_amdgcn_ballot_w64(sum > 256.f)) != 0ull) {
+            asm volatile("");   // keep this rare block a real branch (not speculated)
+            float mx = -INFINITY;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[st][e]);
+            mx = max_halves(mx);
+            const float mnew = fmaxf(m_run, mx * c);
+            const bool raise = mnew > m_run + kFp8RescaleThreshold;
+            const float alpha = raise ? exp2_fast(m_run - mnew) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+            m_run = raise ? mnew : m_run;
+            sum = exps(sacc, m_run == -INFINITY ? 0.f : m_run);
+        }
+        l_run += sum;
+    };
+
+    // Step on tile jt (in ring slot i): this wave's copies of tile jt_ahead,
+    // then, for the tiles of this wave, S^T of both sub-tiles, the mask
+    // (boundary tiles only), the weights and O^T += V^T P^T.
+    auto step = [&](int jt, int jt_ahead, int i) __attribute__((always_inline)) {
+        issue(jt_ahead, i == 0 ? T::STAGES - 1 : i - 1);
+        if (jt >= w_lo && jt <= w_hi) {                // uniform per wave
+            const uint8_t* tl = slot(i);
+            f32x16 sacc[2];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
+#pragma unroll
+                for (int kc = 0; kc < T::KC; ++kc)
+                    sacc[st] = mfma_f8(ld_op(tl + ((st * T::KC + kc) * 2) * 1024), qop[kc], sacc[st]);
+            }
+            if (jt < in_lo || jt > in_hi) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    mask_acc32(sacc[st], rel_lo - jt * T::BN - 32 * st, rel_hi - jt * T::BN - 32 * st);
+            }
+            softmax_tile(sacc);
+#pragma unroll
+            for (int db = 0; db < T::DB; ++db)
+                oacc[db] = mfma_f8(ld_op(tl + (T::KBLK + 2 * db) * 1024), pb, oacc[db]);
+        }
+        sync_step();
+        return next_slot(i);
+    };
+    if (ntiles > 0) {
+        // step s takes the tile congruent to s modulo the range length, as
+        // the 16-bit paired kernel (causal: tile s; a window: rotated)
+        auto tile_at = [&](int s) __attribute__((always_inline)) {
+            if (s >= ntiles) return -1;                    // past the range: no copy
+            int r = (s - tile_lo) % ntiles;
+            r += r < 0 ? ntiles : 0;
+            return tile_lo + r;
+        };
+        for (int s = 0; s < T::AHEAD; ++s) issue(tile_at(s), s);
+        sync_step();
+        int i = 0;
+        for (int s = 0; s < ntiles; ++s) i = step(tile_at(s), tile_at(s + T::AHEAD), i);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // copies of unused tiles still in flight
+
+    // ---- epilogue: O / l * descale_v -> bf16, LSE ------------------------
+    const auto ors = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((char*)p.o + ((long long)b * sq * p.Hq + hq) * D * 2), (short)0, sq * p.Hq * D * 2,
+        0x00020000);
+    const float l_tot = sum_halves(l_run);
+    const float inv = l_tot > 0.f ? p.descale_v / l_tot : 0.f;
+    const int row = r0 + lq;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            u32x2 w;
+            w.x = pack2<true>(oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv);
+            w.y = pack2<true>(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+            const int col = 32 * db + 8 * jj + 4 * g;
+            __builtin_amdgcn_raw_buffer_store_b64(w, ors, (row * p.Hq * D + col) * 2, 0, 0);
+        }
+    if (p.lse != nullptr && g == 0 && row < sq)
+        p.lse[((long long)b * p.Hq + hq) * sq + row] =
+            l_tot > 0.f ? (m_run + log2_fast(l_tot)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+static hipError_t launch_fp8_t(const Fp8Params& p, bool wide, hipStream_t s) {
     const long long nvt = (long long)(p.sk_pad / 64) * p.Hkv * p.B;
     if (nvt > 0) hipLaunchKernelGGL((fa_fp8_vt_kernel<D>), dim3((unsigned)nvt), dim3(256), 0, s, p);
     const long long nblocks = (long long)p.nqt * (p.Hq / p.gw) * p.B;
-    if (nblocks > 0)
-        hipLaunchKernelGGL((fa_fwd_fp8_kernel<D>), dim3((unsigned)nblocks), dim3(kFwdThreads), 0, s, p);
+    if (nblocks > 0) {
+        if (wide)
+            hipLaunchKernelGGL((fa_fwd_fp8_kernel<D>), dim3((unsigned)nblocks), dim3(kFwdThreads), 0, s, p);
+        else
+            hipLaunchKernelGGL((fa_fwd_fp8_paired_kernel<D>), dim3((unsigned)nblocks), dim3(kFwdThreads),
+                               0, s, p);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s) {
-    return d == 128 ? launch_fp8_t<128>(p, s) : launch_fp8_t<64>(p, s);
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool wide, hipStream_t s) {
+    return d == 128 ? launch_fp8_t<128>(p, wide, s) : launch_fp8_t<64>(p, wide, s);
 }
 
 }  // namespace fa

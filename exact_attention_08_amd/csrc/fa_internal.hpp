@@ -56,7 +56,8 @@ struct Fp8Params {
     float descale_v;
     int xcd_groups, gw, bm;
 };
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t s);
+// wide: the one-wave-per-SIMD kernel (64-row waves), else the paired one
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool wide, hipStream_t s);
 
 // Decode split kernel + combine kernel.
 struct DecodeParams {

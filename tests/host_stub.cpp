@@ -51,8 +51,8 @@ hipError_t launch_fwd_wide(const FwdParams& p, int d, bool bf16, bool varlen, hi
     return (hipError_t)g_launch_error;
 }
 
-hipError_t launch_fwd_fp8(const Fp8Params& p, int d, hipStream_t) {
-    record("fp8", d, true, false);
+hipError_t launch_fwd_fp8(const Fp8Params& p, int d, bool wide, hipStream_t) {
+    record(wide ? "fp8_wide" : "fp8_paired", d, true, false);
     g_fp8 = p;
     return (hipError_t)g_launch_error;
 }

@@ -38,6 +38,11 @@ FP8_CASES = [
     ("group16", 1, 16, 1, 130, 130, 128, True, (-1, -1), None, 1.0, 713),
     ("d64_causal_gqa", 2, 8, 2, 300, 300, 64, True, (-1, -1), None, 1.0, 714),
     ("window_left_long", 1, 4, 4, 700, 700, 128, True, (200, -1), None, 0.5, 715),
+    # rows that see more than 2560 keys on average: the wide (64-row) form;
+    # the cases above run on the paired (32-row) form
+    ("wide_causal", 1, 4, 1, 5300, 5300, 128, True, (-1, -1), None, 1.0, 716),
+    ("wide_noncausal_d64", 1, 2, 1, 100, 2700, 64, False, (-1, -1), None, 1.0, 717),
+    ("wide_window_two_sided", 1, 2, 2, 200, 3000, 128, False, (1500, 1100), None, 1.0, 718),
 ]
 
 

@@ -170,11 +170,16 @@ def test_varlen_params(lib, stub, maxq, maxk, kernel):
 def test_fp8_params(lib, stub):
     st = lib.fa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 300, 333, 128, 1, -1, -1, -0.1,
                         0.5, 0.25, 2.0, OTHER, 1 << 20, None)
-    assert st == FA_OK and stub.kernel == "fp8"
+    assert st == FA_OK and stub.kernel == "fp8_paired"
     p = stub.fp8()
-    assert (p["sk_pad"], p["vt"], p["bm"], p["nqt"]) == (384, OTHER, 64, 5)
+    assert (p["sk_pad"], p["vt"], p["bm"], p["nqt"]) == (384, OTHER, 32, 10)
     assert p["qsign"] == 0x80808080 and p["descale_v"] == 2.0
     assert math.isclose(p["c"], 0.1 * 0.5 * 0.25 * LOG2E, rel_tol=2 ** -21)
+    # rows that see more than 2560 keys on average: the wide form
+    stub.set()
+    assert lib.fa_fwd_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6000, 6000, 128, 1, -1, -1, 0.1,
+                          0.5, 0.25, 2.0, OTHER, 1 << 30, None) == FA_OK
+    assert stub.kernel == "fp8_wide" and (stub.fp8()["bm"], stub.fp8()["nqt"]) == (64, 94)
     need = lib.fa_fwd_fp8_workspace_bytes(2, 2, 333, 128)
     assert need == 2 * 2 * 128 * 384
     stub.set()
