@@ -219,8 +219,9 @@ fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, f
     p.cu_q = nullptr; p.cu_k = nullptr;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.G = Hq / Hkv;
     p.Sq = Sq; p.Sk = Sk;
+    const bool wide = fa::fwd_use_wide(Sq, Sk, causal, window_left, window_right);
     p.gw = fa::fwd_heads_per_wg(p.G);
-    p.bm = fa::fwd_rows_per_wg(p.G, fa::kFwdWideWaveRows);
+    p.bm = fa::fwd_rows_per_wg(p.G, wide ? fa::kFwdWideWaveRows : fa::kFwdWaveRows);
     p.nqt = (Sq + p.bm - 1) / p.bm;
     p.q_tok_stride = (long long)Hq * d;
     p.kv_tok_stride = (long long)Hkv * d;
@@ -237,7 +238,8 @@ fa_status_t fa_fwd_mod(const void* q, const void* k, const void* v, void* out, f
     }
     if ((long long)p.nqt * (Hq / p.gw) * B * fa::kFwdThreads > kMaxGridThreads)
         return fail(FA_ERR_INVALID_ARG, "problem too large for one launch");
-    return launch_status(fa::launch_fwd_wide(p, d, dtype == FA_BF16, false, stream));
+    return launch_status(wide ? fa::launch_fwd_wide(p, d, dtype == FA_BF16, false, stream)
+                              : fa::launch_fwd(p, d, dtype == FA_BF16, false, stream));
 }
 
 fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,

@@ -90,10 +90,20 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, r);
 }
 
-template <int D, bool BF16, bool VARLEN>
+// MOD selects the score modifiers (padded forward only; bit 0: ALiBi, bit
+// 1: soft-capping), as in the wide kernel (fa_fwd_wide.hip): the explainer
+// page's "Variants you may meet" (a bias term added to the scores; capped
+// scores need explicit kernel support).  The exponent of score s of key j in
+// row i (log2 units, before the running max) becomes
+//     u = cap log2(e) tanh(scale s / cap) - slope log2(e) |pos_i - j|
+// (each part only when enabled); tanh(y) = 1 - 2 / (exp2(2 y log2 e) + 1).
+// MOD = 0 compiles to the plain kernel.
+template <int D, bool BF16, bool VARLEN, int MOD>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void fa_fwd_kernel(FwdParams p) {
     using T = FwdGeo<D>;
+    constexpr bool ALIBI = (MOD & 1) != 0, SOFTCAP = (MOD & 2) != 0;
+    static_assert(!(VARLEN && MOD != 0), "score modifiers are padded-only");
     constexpr int TE = T::TE;
     // K slots 0 .. STAGES-1, then V slots; after the key loop the first
     // 32 x D rows per wave stage the output
@@ -304,6 +314,31 @@ void fa_fwd_kernel(FwdParams p) {
     }
 
     u32x4 pb[T::KK];                           // the weights of a tile as 16-bit B operands
+    const float slope2 = ALIBI ? p.alibi[hq] * kLog2e : 0.f;
+    const float sc_k = p.sc_k, sc_c = p.sc_c;
+    // exp2 argument of element e of a tile with running max m; tb is the
+    // distance (key - row position) of the lane's element 0 (ALiBi only)
+    auto earg = [&](const f32x16& sacc, int e, float tb, float m) __attribute__((always_inline)) {
+        const float sv = sacc[e];
+        if constexpr (MOD == 0) {
+            return fmaf(sv, c, -m);
+        } else {
+            float v;
+            if constexpr (SOFTCAP) {
+                const float ex = exp2_fast(sv * sc_k);
+                const float th = fmaf(-2.f, __builtin_amdgcn_rcpf(ex + 1.f), 1.f);
+                v = sv == -INFINITY ? -INFINITY : fmaf(th, sc_c, -m);   // masked stays masked
+            } else {
+                v = fmaf(sv, c, -m);
+            }
+            if constexpr (ALIBI)
+                v = fmaf(-slope2, fabsf(tb + (float)(8 * (e >> 2) + (e & 3))), v);
+            return v;
+        }
+    };
+    auto tile_base = [&](int jt) __attribute__((always_inline)) {
+        return ALIBI ? (float)(4 * g - lq + (jt * T::BN - r0 - delta)) : 0.f;
+    };
 
     // ---- softmax of one tile ------------------------------------------------
     // The running max m is lazy: a row's weights are exp2(S c - m) with the
@@ -319,11 +354,11 @@ void fa_fwd_kernel(FwdParams p) {
     // key reproduces that key's V row), LSE by the sum of the fp32 values
     // (16-bit rounding would bias it by up to 2^-9).  Both are summed as
     // trees (no long chains of dependent adds).
-    auto exps = [&](const f32x16& sacc) __attribute__((always_inline)) {
+    auto exps = [&](const f32x16& sacc, float tb) __attribute__((always_inline)) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
         float x[16], r2[2] = {0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = exp2_fast(fmaf(sacc[e], c, -m_use));
+        for (int e = 0; e < 16; ++e) x[e] = exp2_fast(earg(sacc, e, tb, m_use));
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
@@ -336,15 +371,21 @@ void fa_fwd_kernel(FwdParams p) {
             for (int e = 0; e < w; ++e) x[e] += x[e + w];
         return f32x2{x[0], r2[0] + r2[1]};
     };
-    auto refresh = [&](const f32x16& sacc) __attribute__((always_inline)) {
+    auto refresh = [&](const f32x16& sacc, float tb) __attribute__((always_inline)) {
         asm volatile("");   // keep this rare block a real branch (not speculated)
+        f32x16 u;                                  // scores (plain) or exponents u (modifiers)
+        if constexpr (MOD == 0) {
+            u = sacc;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) u[e] = earg(sacc, e, tb, 0.f);
+        }
         float m4[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-            m4[q4] = fmaxf(fmaxf(sacc[4 * q4], sacc[4 * q4 + 1]),
-                           fmaxf(sacc[4 * q4 + 2], sacc[4 * q4 + 3]));
+            m4[q4] = fmaxf(fmaxf(u[4 * q4], u[4 * q4 + 1]), fmaxf(u[4 * q4 + 2], u[4 * q4 + 3]));
         const float mx = max_halves(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-        const float mnew = fmaxf(m_run, mx * c);   // -inf stays -inf (c > 0)
+        const float mnew = fmaxf(m_run, MOD == 0 ? mx * c : mx);   // -inf stays -inf (c > 0)
         const bool raise = mnew > m_run + kRescaleThreshold;
         const float alpha = raise ? exp2_fast(m_run - mnew) : 1.f;
         l_run *= alpha;
@@ -354,13 +395,14 @@ void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
         m_run = raise ? mnew : m_run;
-        return exps(sacc);
+        return exps(sacc, tb);
     };
-    auto softmax_tile = [&](const f32x16& sacc) __attribute__((always_inline)) {
+    auto softmax_tile = [&](const f32x16& sacc, int jt) __attribute__((always_inline)) {
         const bool first = m_run == -INFINITY;
-        f32x2 sums = exps(sacc);
+        const float tb = tile_base(jt);
+        f32x2 sums = exps(sacc, tb);
         if ((__builtin_amdgcn_ballot_w64(first) | __builtin_amdgcn_ballot_w64(sums.x > 256.f)) != 0ull)
-            sums = refresh(sacc);
+            sums = refresh(sacc, tb);
         l_run += sums.x;
         lr_run += sums.y;
     };
@@ -406,7 +448,7 @@ void fa_fwd_kernel(FwdParams p) {
             f32x16 cur = qk(i);
             if (jt < in_lo || jt > in_hi)
                 mask_acc32(cur, rel_lo - jt * T::BN, rel_hi - jt * T::BN);
-            softmax_tile(cur);
+            softmax_tile(cur, jt);
             u32x4 vq[T::KK][T::DB];
             load_v(vq, i);
 #pragma unroll
@@ -418,6 +460,37 @@ void fa_fwd_kernel(FwdParams p) {
         sync_step();
         return next_slot(i);
     };
+    // ALiBi: the bias grows toward each row's own position, so in key order
+    // a row's running max would climb tile after tile (and take the rare
+    // path on most steps).  Instead the max starts at the row's largest
+    // modified score in the tile holding the wave's last diagonal key,
+    // loaded straight from memory here: a value the row attains, so the
+    // running max never exceeds the true one.  (A zero slope keeps the plain
+    // order of maxima, hence the plain result bit for bit.)
+    if constexpr (ALIBI) {
+        if (ntiles > 0 && slope2 != 0.f && w_lo <= w_hi) {          // uniform per wave
+            const int dt = min(max((r0 + T::R - 1 + delta) / T::BN, w_lo), w_hi);
+            const auto krs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(kseq + (long long)dt * (T::BN * tok_bytes_kv)), (short)0,
+                min(sk - dt * T::BN, T::BN) * tok_bytes_kv, 0x00020000);
+            f32x16 acc;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks) {
+                const u32x4 kq = __builtin_amdgcn_raw_buffer_load_b128(
+                    krs, (lane & 31) * tok_bytes_kv + (2 * ks + g) * 16, 0, 0);
+                acc = mfma32x32x16<BF16>(kq, qreg[ks], acc);
+            }
+            mask_acc32(acc, rel_lo - dt * T::BN, rel_hi - dt * T::BN);
+            const float tb = tile_base(dt);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, earg(acc, e, tb, 0.f));
+            m_run = max_halves(mx);
+        }
+    }
+
     if (ntiles > 0) {
         // Step s takes tile tile_lo + (s - tile_lo) mod ntiles, the tile
         // congruent to s modulo the range length.  With a causal mask
@@ -481,22 +554,32 @@ void fa_fwd_kernel(FwdParams p) {
     }
 }
 
-template <int D, bool BF16, bool VARLEN>
+template <int D, bool BF16, bool VARLEN, int MOD>
 static hipError_t launch_one(const FwdParams& p, hipStream_t s) {
     const long long nblocks = (long long)p.nqt * (p.Hq / p.gw) * p.B;
     if (nblocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN>), dim3((unsigned)nblocks),
+    hipLaunchKernelGGL((fa_fwd_kernel<D, BF16, VARLEN, MOD>), dim3((unsigned)nblocks),
                        dim3(kFwdThreads), 0, s, p);
     return hipGetLastError();
 }
 
+template <int D, bool BF16>
+static hipError_t launch_padded(const FwdParams& p, hipStream_t s) {
+    switch (p.mod) {
+        case 1: return launch_one<D, BF16, false, 1>(p, s);
+        case 2: return launch_one<D, BF16, false, 2>(p, s);
+        case 3: return launch_one<D, BF16, false, 3>(p, s);
+        default: return launch_one<D, BF16, false, 0>(p, s);
+    }
+}
+
 hipError_t launch_fwd(const FwdParams& p, int d, bool bf16, bool varlen, hipStream_t s) {
     if (varlen) {
-        if (d == 128) return bf16 ? launch_one<128, true, true>(p, s) : launch_one<128, false, true>(p, s);
-        return bf16 ? launch_one<64, true, true>(p, s) : launch_one<64, false, true>(p, s);
+        if (d == 128) return bf16 ? launch_one<128, true, true, 0>(p, s) : launch_one<128, false, true, 0>(p, s);
+        return bf16 ? launch_one<64, true, true, 0>(p, s) : launch_one<64, false, true, 0>(p, s);
     }
-    if (d == 128) return bf16 ? launch_one<128, true, false>(p, s) : launch_one<128, false, false>(p, s);
-    return bf16 ? launch_one<64, true, false>(p, s) : launch_one<64, false, false>(p, s);
+    if (d == 128) return bf16 ? launch_padded<128, true>(p, s) : launch_padded<128, false>(p, s);
+    return bf16 ? launch_padded<64, true>(p, s) : launch_padded<64, false>(p, s);
 }
 
 }  // namespace fa

@@ -2,7 +2,7 @@
 // 64 query rows per wave, one wave per SIMD.  Used where query rows see
 // many keys (more than kFwdWideMinKeys on average), where reading each K/V
 // operand once for 64 rows (half the LDS bytes per MFMA of 32-row waves)
-// pays for having one instruction stream per SIMD, and for the score
+// pays for having one instruction stream per SIMD, with or without score
 // modifiers (fa_fwd_mod).  Rows that see fewer keys go to fa_fwd.hip's
 // paired kernel.
 //

@@ -129,7 +129,7 @@ hipError_t decode_scratch(void** ptr);
 // Kernel tile geometry, shared with the host for grid sizing.
 constexpr int kFwdWaveRows = 32;      // query rows per wave of the 16-bit forward kernel
 constexpr int kFwdWideWaveRows = 64;  // rows per wave (two 32-row halves) of the wide 16-bit
-                                      // kernel and of the 8-bit kernel
+                                      // and 8-bit kernels
 constexpr int kFwdWaves = 4;          // waves per forward work-group (one per SIMD)
 constexpr int kFwdThreads = 64 * kFwdWaves;
 // A forward work-group covers gw query heads that share one K/V head (the
@@ -137,10 +137,10 @@ constexpr int kFwdThreads = 64 * kFwdWaves;
 // waves need the same K/V tiles at the same steps.
 inline int fwd_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 inline int fwd_rows_per_wg(int G, int wave_rows) { return wave_rows * kFwdWaves / fwd_heads_per_wg(G); }
-// The 16-bit forward runs on one of two kernels, chosen by how many keys a
-// query row sees on average: the paired kernel (32-row waves, three
-// work-groups per CU) up to kFwdWideMinKeys, the wide kernel (64-row waves)
-// beyond and for every call with score modifiers.  sq, sk are the row and
+// Each forward (16-bit with or without score modifiers, 8-bit) runs on one
+// of two kernels, chosen by how many keys a query row sees on average: the
+// paired kernel (32-row waves, three work-groups per CU) up to
+// kFwdWideMinKeys, the wide kernel (64-row waves) beyond.  sq, sk are the row and
 // key counts (packed: their host bounds).  Under a causal mask the rows of
 // the last min(sq, sk) positions see a prefix growing to sk keys, on
 // average sk - min(sq, sk)/2; a left window bounds a row's keys by

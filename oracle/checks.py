@@ -37,23 +37,6 @@ def to_f64(t) -> np.ndarray:
     return np.asarray(t, dtype=np.float64)
 
 
-def kernels_agree(a, b, v, dtype: str) -> tuple[bool, float, int]:
-    """Two 16-bit outputs of the same attention from kernels that take the
-    keys in different orders.  With a lazily raised running max the 16-bit
-    weights are rounded relative to different maxima, so they may differ by
-    one rounding each (2^-8 relative in bf16, 2^-11 in fp16); then each O
-    element, a weighted mean of V rows, may differ by twice that times
-    max |V|, plus one output rounding each.  Returns (within that bound,
-    max |a - b|, number of elements that differ at all)."""
-    a = a.detach().to("cpu").float()
-    b = b.detach().to("cpu").float()
-    eps = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -11
-    vmax = float(v.detach().abs().max())
-    bound = 2 * eps * vmax + torch.from_numpy(ulp(a.numpy(), dtype)).float()
-    diff = (a - b).abs()
-    return bool((diff <= bound).all()), float(diff.max()), int((diff > 0).sum())
-
-
 def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype: str, label: str = "") -> dict:
     """Assert parity; return the statistics (max errors, counts)."""
     og, orf = to_f64(o_gpu), to_f64(o_ref)

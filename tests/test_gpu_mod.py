@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from exact_attention_08_amd import fa, synth
-from oracle.checks import compare, kernels_agree, log
+from oracle.checks import compare, log
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +41,14 @@ MOD_CASES = [
      611),
     ("softcap5_group16", 1, 16, 1, 130, 130, 128, "bf16", True, (-1, -1), 0.3, 5.0, False, 1.0, 612),
     ("alibi_sq_gt_sk", 1, 4, 2, 300, 77, 128, "bf16", True, (-1, -1), None, 0.0, True, 1.0, 613),
+    # rows that see more than 2560 keys on average: the wide kernel's
+    # modifier variants (the cases above run on the paired kernel)
+    ("wide_alibi_causal", 1, 4, 2, 5300, 5300, 128, "bf16", True, (-1, -1), None, 0.0, True, 1.0,
+     614),
+    ("wide_softcap_noncausal", 1, 2, 1, 100, 2700, 128, "bf16", False, (-1, -1), None, 30.0, False,
+     1.0, 615),
+    ("wide_both_d64_fp16", 1, 2, 2, 200, 3000, 64, "fp16", False, (-1, -1), None, 20.0, True, 1.0,
+     616),
 ]
 
 
@@ -59,20 +67,20 @@ def test_mod_matches_oracle(case):
     log(compare(o, lse, ro, rl, dt, name), name)
 
 
-def test_zero_slopes_give_the_plain_result():
-    """ALiBi with all-zero slopes adds exact zeros.  The modifier kernel and
-    the plain forward are different kernels (their fp32 sums are added in
-    different orders), so their results agree to rounding: O within one
-    output ulp, LSE within a few fp32 ulps."""
-    print("[case] fwd_mod zero slopes", flush=True)
-    q, k, v = synth.gen_padded(609, 2, 8, 2, 300, 300, 128, "bf16")
+@pytest.mark.parametrize("shape", [(2, 8, 2, 300, 300), (1, 4, 2, 5300, 5300)],
+                         ids=["paired", "wide"])
+def test_zero_slopes_give_the_plain_result(shape):
+    """ALiBi with all-zero slopes adds exact zeros and keeps the plain order
+    of running maxima (the max initialisation is skipped), so on either
+    kernel the modifier path gives the plain forward's bits."""
+    B, Hq, Hkv, Sq, Sk = shape
+    print(f"[case] fwd_mod zero slopes {shape}", flush=True)
+    q, k, v = synth.gen_padded(609, B, Hq, Hkv, Sq, Sk, 128, "bf16")
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o1, l1 = fa.fwd(qd, kd, vd, causal=True)
-    o2, l2 = fa.fwd_mod(qd, kd, vd, causal=True, alibi_slopes=torch.zeros(8, device=DEV))
+    o2, l2 = fa.fwd_mod(qd, kd, vd, causal=True, alibi_slopes=torch.zeros(Hq, device=DEV))
     torch.cuda.synchronize()
-    d_o = (o1.float() - o2.float()).abs()
-    assert torch.all(d_o <= 2.0 ** -7 * torch.maximum(o1.float().abs(), o2.float().abs()) + 1e-6)
-    assert ((l1 - l2).abs() / l2.abs().clamp_min(1.0)).max().item() <= 8 * 2.0 ** -23
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
 def test_no_modifier_is_the_plain_forward():
@@ -89,26 +97,15 @@ def test_no_modifier_is_the_plain_forward():
     (2, 8, 2, 700, 700, 128, "bf16", True, (100, 0)),
     (1, 4, 4, 530, 610, 64, "fp16", False, (90, 40)),
 ], ids=["causal_gqa_d128", "two_sided_sq_lt_sk_d64"])
-def test_window_paired_kernel_agrees_with_the_wide_kernel(shape):
-    """A sliding window sends fa_fwd to the paired kernel (32-row waves,
-    three work-groups per CU), which takes a window's key tiles in a rotated
-    order; ALiBi with zero slopes runs the wide modifier kernel (64-row
-    waves), whose masked steps take the plain arithmetic in key order.  The
-    key order (and with it the running maxima the 16-bit weights are rounded
-    against) differs, so O agrees within the bound of kernels_agree and LSE
-    to a few fp32 ulp."""
+def test_zero_slope_window_is_the_plain_forward(shape):
+    """Sliding windows (the paired kernel, key tiles in rotated order): the
+    modifier path with zero ALiBi slopes gives the plain forward's bits."""
     B, Hq, Hkv, Sq, Sk, d, dt, causal, window = shape
-    print(f"[case] paired vs wide kernel {shape}", flush=True)
+    print(f"[case] zero-slope window {shape}", flush=True)
     q, k, v = synth.gen_padded(620, B, Hq, Hkv, Sq, Sk, d, dt)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     o1, l1 = fa.fwd(qd, kd, vd, causal=causal, window=window)
     o2, l2 = fa.fwd_mod(qd, kd, vd, causal=causal, window=window,
                         alibi_slopes=torch.zeros(Hq, device=DEV))
     torch.cuda.synchronize()
-    ok, dmax, ndiff = kernels_agree(o1, o2, vd, dt)
-    print(f"[parity] paired vs wide: {ndiff} of {o1.numel()} O elements differ, max {dmax:.3g}",
-          flush=True)
-    assert ok
-    assert torch.equal(torch.isneginf(l1), torch.isneginf(l2))
-    fin = torch.isfinite(l1)
-    assert float((l1[fin] - l2[fin]).abs().max()) <= 4.0 * 2.0 ** -20 * max(1.0, float(l1[fin].abs().max()))
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

@@ -133,14 +133,18 @@ def test_fp16_and_lse_pointer(lib, stub):
     assert p["bf16"] == 0 and p["lse"] == 0
 
 
-def test_fwd_mod_uses_the_wide_kernel(lib, stub):
+def test_fwd_mod_kernel_choice_and_constants(lib, stub):
     st = lib.fa_fwd_mod(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 300, 300, 128, 1, -1, -1, 0.1,
                         OTHER, 30.0, 0, None)
-    assert st == FA_OK and stub.kernel == "wide"
+    assert st == FA_OK and stub.kernel == "paired"
     p = stub.fwd()
-    assert p["mod"] == 3 and p["alibi"] == OTHER and p["bm"] == 64
+    assert p["mod"] == 3 and p["alibi"] == OTHER and p["bm"] == 32
     assert math.isclose(p["sc_k"], 2 * 0.1 * LOG2E / 30.0, rel_tol=2 ** -22)
     assert math.isclose(p["sc_c"], 30.0 * LOG2E, rel_tol=2 ** -22)
+    # rows that see more than 2560 keys on average: the wide kernel
+    assert lib.fa_fwd_mod(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 6000, 6000, 128, 1, -1, -1, 0.1,
+                          OTHER, 30.0, 0, None) == FA_OK
+    assert stub.kernel == "wide" and stub.fwd()["mod"] == 3 and stub.fwd()["bm"] == 64
     # soft-capping alone, ALiBi alone
     assert lib.fa_fwd_mod(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 300, 300, 128, 1, -1, -1, 0.1,
                           None, 5.0, 0, None) == FA_OK
@@ -148,7 +152,7 @@ def test_fwd_mod_uses_the_wide_kernel(lib, stub):
     assert lib.fa_fwd_mod(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 300, 300, 128, 1, -1, -1, 0.1,
                           OTHER, 0.0, 0, None) == FA_OK
     assert stub.fwd()["mod"] == 1
-    # no modifier: the plain forward (here the paired kernel)
+    # no modifier: the plain forward
     assert lib.fa_fwd_mod(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 300, 300, 128, 1, -1, -1, 0.1,
                           None, 0.0, 0, None) == FA_OK
     assert stub.kernel == "paired" and stub.fwd()["mod"] == 0
