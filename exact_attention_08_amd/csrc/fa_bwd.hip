@@ -199,6 +199,12 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             kop[ks] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
             vop[ks] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
         }
+        // Wait for these loads here, before any tile copy is issued: the
+        // compiler does not see the copies (they are written in asm), and a
+        // wait it placed at the first use, inside the loop, would run on
+        // every step and drain every copy in flight.
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) asm volatile("" ::"v"(kop[ks]), "v"(vop[ks]));
     }
 
     // ---- copies of step s: Q and dO rows of query block qb_a + s % nqb of
