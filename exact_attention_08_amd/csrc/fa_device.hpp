@@ -101,22 +101,31 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, uint32_t hi_src
     return __builtin_amdgcn_perm(hi_src, lo_src, SEL_HI ? 0x07060302u : 0x05040100u);
 }
 
-// (acc + lo) + hi of a dword holding two 16-bit values, on the plain VALU:
-// a bf16 value is the high half of its fp32 value, so a mask and a shift
-// give both exactly; fp16 values are converted.  (v_dot2 against (1, 1)
-// would be one instruction, but it issues through the matrix pipe and
+// The two 16-bit values of a dword as fp32 (lo, hi), on the plain VALU: a
+// bf16 value is the high half of its fp32 value, so a mask and a shift give
+// both exactly; fp16 values are converted.  (v_dot2 against (1, 1) would sum
+// a pair in one instruction, but it issues through the matrix pipe and
 // waits behind the MFMAs it should overlap.)
 template <bool BF16>
+__device__ __forceinline__ f32x2 halves16(uint32_t packed) {
+    if constexpr (BF16)
+        return f32x2{__builtin_bit_cast(float, packed << 16), __builtin_bit_cast(float, packed & 0xffff0000u)};
+    else
+        return f32x2{(float)__builtin_bit_cast(_Float16, (uint16_t)(packed & 0xffffu)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)(packed >> 16))};
+}
+// (acc + lo) + hi
+template <bool BF16>
 __device__ __forceinline__ float sum2_16(uint32_t packed, float acc) {
-    float lo, hi;
-    if constexpr (BF16) {
-        lo = __builtin_bit_cast(float, packed << 16);
-        hi = __builtin_bit_cast(float, packed & 0xffff0000u);
-    } else {
-        lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed & 0xffffu));
-        hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(packed >> 16));
-    }
-    return (acc + lo) + hi;
+    const f32x2 h = halves16<BF16>(packed);
+    return (acc + h.x) + h.y;
+}
+// the first pair of such a sum (weights are >= +0, so starting from a zero
+// would add nothing: the same bits, one instruction less)
+template <bool BF16>
+__device__ __forceinline__ float sum2_16_first(uint32_t packed) {
+    const f32x2 h = halves16<BF16>(packed);
+    return h.x + h.y;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

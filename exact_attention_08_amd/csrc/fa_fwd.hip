@@ -356,14 +356,14 @@ void fa_fwd_kernel(FwdParams p) {
     // trees (no long chains of dependent adds).
     auto exps = [&](const f32x16& sacc, float tb) __attribute__((always_inline)) {
         const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float x[16], r2[2] = {0.f, 0.f};
+        float x[16], r2[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = exp2_fast(earg(sacc, e, tb, m_use));
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
             pb[e >> 3][(e & 7) >> 1] = pk;
-            r2[(e >> 1) & 1] = sum2_16<BF16>(pk, r2[(e >> 1) & 1]);
+            r2[(e >> 1) & 1] = e < 4 ? sum2_16_first<BF16>(pk) : sum2_16<BF16>(pk, r2[(e >> 1) & 1]);
         }
 #pragma unroll
         for (int w = 8; w >= 1; w >>= 1)

@@ -446,14 +446,14 @@ void fa_fwd_wide_kernel(FwdParams p) {
     auto exps_plain = [&](int h) __attribute__((always_inline)) {
         const float m_use = m_run[h] == -INFINITY ? 0.f : m_run[h];
         const float tb = tile_base(h);
-        float x[16], r2[2] = {0.f, 0.f};
+        float x[16], r2[2];
 #pragma unroll
         for (int e = 0; e < 16; ++e) x[e] = exp2_fast(earg(h, e, tb, m_use));
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
             pb[h][e >> 3][(e & 7) >> 1] = pk;
-            r2[(e >> 1) & 1] = sum2_16<BF16>(pk, r2[(e >> 1) & 1]);
+            r2[(e >> 1) & 1] = e < 4 ? sum2_16_first<BF16>(pk) : sum2_16<BF16>(pk, r2[(e >> 1) & 1]);
         }
 #pragma unroll
         for (int w = 8; w >= 1; w >>= 1)
@@ -536,7 +536,7 @@ void fa_fwd_wide_kernel(FwdParams p) {
         const float m_use = first ? 0.f : m_run[hp];
         const float tb = tile_base(hp);
         js[hs] = jt;
-        float x[16], a[8], bsum[4], r2[2] = {0.f, 0.f};
+        float x[16], a[8], bsum[4], r2[2];
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             if (i < T::KS) {
@@ -561,7 +561,8 @@ void fa_fwd_wide_kernel(FwdParams p) {
                     a[j] = x[2 * j] + x[2 * j + 1];
                 }
                 if ((2 * j + 1) / EPS + 2 == i) {
-                    r2[j & 1] = sum2_16<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
+                    r2[j & 1] = j < 2 ? sum2_16_first<BF16>(pb[hp][j >> 2][j & 3])
+                                      : sum2_16<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
                     pin(r2[j & 1]);
                     if (j & 1) bsum[j >> 1] = a[j - 1] + a[j];
                 }
@@ -577,7 +578,8 @@ void fa_fwd_wide_kernel(FwdParams p) {
                 a[j] = x[2 * j] + x[2 * j + 1];
             }
             if ((2 * j + 1) / EPS + 2 >= NS) {
-                r2[j & 1] = sum2_16<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
+                r2[j & 1] = j < 2 ? sum2_16_first<BF16>(pb[hp][j >> 2][j & 3])
+                                  : sum2_16<BF16>(pb[hp][j >> 2][j & 3], r2[j & 1]);
                 if (j & 1) bsum[j >> 1] = a[j - 1] + a[j];
             }
         }
