@@ -817,8 +817,17 @@ void fa_fwd_fp8_paired_kernel(Fp8Params p) {
         };
         for (int s = 0; s < T::AHEAD; ++s) issue(tile_at(s), s);
         sync_step();
+        // the tiles of steps s and s + AHEAD, advanced by one per step with
+        // the wrap of the rotated order (no division in the loop)
+        const int tile_end = tile_lo + ntiles;
+        int jt = tile_at(0);
+        int ja = T::AHEAD < ntiles ? tile_at(T::AHEAD) : tile_lo;
         int i = 0;
-        for (int s = 0; s < ntiles; ++s) i = step(tile_at(s), tile_at(s + T::AHEAD), i);
+        for (int s = 0; s < ntiles; ++s) {
+            i = step(jt, s + T::AHEAD < ntiles ? ja : -1, i);
+            jt = jt + 1 == tile_end ? tile_lo : jt + 1;
+            ja = ja + 1 == tile_end ? tile_lo : ja + 1;
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // copies of unused tiles still in flight
 
