@@ -103,9 +103,7 @@ __device__ __forceinline__ uint32_t pick_halves(uint32_t lo_src, uint32_t hi_src
 
 // The two 16-bit values of a dword as fp32 (lo, hi), on the plain VALU: a
 // bf16 value is the high half of its fp32 value, so a mask and a shift give
-// both exactly; fp16 values are converted.  (v_dot2 against (1, 1) would sum
-// a pair in one instruction, but it issues through the matrix pipe and
-// waits behind the MFMAs it should overlap.)
+// both exactly; fp16 values are converted.
 template <bool BF16>
 __device__ __forceinline__ f32x2 halves16(uint32_t packed) {
     if constexpr (BF16)
@@ -126,6 +124,23 @@ template <bool BF16>
 __device__ __forceinline__ float sum2_16_first(uint32_t packed) {
     const f32x2 h = halves16<BF16>(packed);
     return h.x + h.y;
+}
+
+// acc + lo + hi by one v_dot2c_f32 against (1, 1).  It issues through the
+// matrix pipe: where one wave per SIMD interleaves it with its own MFMAs it
+// waits behind them, where several independent waves share the SIMD it is
+// the cheaper form (one instruction per pair instead of four).
+template <bool BF16>
+__device__ __forceinline__ float sum2_16_dot(uint32_t packed, float acc) {
+    if constexpr (BF16) {
+        typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
+                                               __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+    } else {
+        typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), __builtin_bit_cast(f16x2_t, 0x3c003c00u),
+                                      acc, false);
+    }
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

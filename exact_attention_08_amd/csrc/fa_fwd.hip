@@ -363,7 +363,7 @@ void fa_fwd_kernel(FwdParams p) {
         for (int e = 0; e < 16; e += 2) {
             const uint32_t pk = pack2<BF16>(x[e], x[e + 1]);
             pb[e >> 3][(e & 7) >> 1] = pk;
-            r2[(e >> 1) & 1] = e < 4 ? sum2_16_first<BF16>(pk) : sum2_16<BF16>(pk, r2[(e >> 1) & 1]);
+            r2[(e >> 1) & 1] = sum2_16_dot<BF16>(pk, e < 4 ? 0.f : r2[(e >> 1) & 1]);
         }
 #pragma unroll
         for (int w = 8; w >= 1; w >>= 1)
