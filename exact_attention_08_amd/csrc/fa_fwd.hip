@@ -243,12 +243,14 @@ void fa_fwd_kernel(FwdParams p) {
     }
     const char* kseq = (const char*)p.k + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
     const char* vseq = (const char*)p.v + (k_tok0 * p.kv_tok_stride + (long long)hkv * D) * 2;
-    // Tiles outside [tile_lo, tile_last] get zero records: their loads write
-    // zeros to LDS without touching memory (keeps per-step load counts fixed).
-    auto tile_rsrc = [&](const char* base, int jt) __attribute__((always_inline)) {
-        const bool valid = jt >= tile_lo && jt <= tile_last;
-        const int rows = valid ? min(sk - jt * T::BN, T::BN) : 0;
-        return make_rsrc(base + (long long)jt * (T::BN * tok_bytes_kv), rows * tok_bytes_kv);
+    // Bytes of tile jt's rows; callers pass a tile of [tile_lo, tile_last]
+    // or -1, which gets a zero record: its loads write zeros to LDS without
+    // touching memory (keeps per-step load counts fixed).
+    auto tile_bytes = [&](int jt) __attribute__((always_inline)) {
+        return jt >= 0 ? min(sk - jt * T::BN, T::BN) * tok_bytes_kv : 0;
+    };
+    auto tile_rsrc = [&](const char* base, int jt, int bytes) __attribute__((always_inline)) {
+        return make_rsrc(base + (long long)jt * (T::BN * tok_bytes_kv), bytes);
     };
     // ring slot i of K and of V (tile jt sits in slot (jt - tile_lo) % STAGES;
     // the steps carry that slot number instead of dividing)
@@ -259,7 +261,8 @@ void fa_fwd_kernel(FwdParams p) {
     };
     // this wave's LPS copies of tile pair jt into ring slot i
     auto issue = [&](int jt, int i) __attribute__((always_inline)) {
-        const i32x4 krs = tile_rsrc(kseq, jt), vrs = tile_rsrc(vseq, jt);
+        const int bytes = tile_bytes(jt);
+        const i32x4 krs = tile_rsrc(kseq, jt, bytes), vrs = tile_rsrc(vseq, jt, bytes);
         const uint32_t kdst = lds_addr(kslot(i)), vdst = lds_addr(vslot(i));
 #pragma unroll
         for (int l = 0; l < T::LPS; ++l) {
