@@ -128,6 +128,17 @@ __device__ __forceinline__ u32x4 t_operand(const uint16_t* tile, int kk, int db,
 // Accumulator element e of a 32x32 MFMA result sits at row 8*(e/4) +
 // 4*(lane/32) + e%4 of the 32-row block: its offset without the lane term.
 __device__ __forceinline__ constexpr int acc_row(int e) { return 8 * (e >> 2) + (e & 3); }
+// The bits of a visibility word that acc_row(0..15) select.
+constexpr uint32_t kAccRowBits = 0x0f0f0f0fu;
+// true when every lane of the wave sees all 16 of its elements: the block
+// needs no mask (under a causal mask all blocks off the diagonal)
+__device__ __forceinline__ bool block_unmasked(uint32_t vis) {
+    return __builtin_amdgcn_ballot_w64((vis & kAccRowBits) != kAccRowBits) == 0ull;
+}
+template <bool B>
+struct mask_c {
+    static constexpr bool value = B;
+};
 
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
@@ -284,27 +295,37 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const int e_lo = tb - t_hi, e_hi = tb - t_lo;   // visible iff e_lo <= acc_row(e) <= e_hi
             const uint32_t vis = j < sk ? vis_bits(e_lo, e_hi) : 0u;
             u32x4 pp[2], pds[2];
+            auto weights = [&](auto maskc) __attribute__((always_inline)) {
+                // (distinct markers keep the compiler from hoisting the two
+                // versions' common arithmetic above the branch, which would
+                // hold all 32 intermediate values at once)
+                if constexpr (decltype(maskc)::value) asm volatile("; masked block");
+                else asm volatile("; unmasked block");
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * q4 + 4 * g);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 8 * q4 + 4 * g);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * q4 + 4 * g);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 8 * q4 + 4 * g);
 #pragma unroll
-                for (int e2 = 0; e2 < 4; e2 += 2) {
-                    const int e = 4 * q4 + e2;
-                    float pv[2], dv2[2];
+                    for (int e2 = 0; e2 < 4; e2 += 2) {
+                        const int e = 4 * q4 + e2;
+                        float pv[2], dv2[2];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        // LSE in log2 units, +inf for a row with no
-                        // visible key (weights exp2(x - inf) = 0, never inf)
-                        const float x = exp2_fast(fmaf(sacc[e + u], p.c2, -l4[e2 + u]));
-                        pv[u] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) &
-                                                              bit_mask(vis, acc_row(e + u)));
-                        dv2[u] = pv[u] * (dpacc[e + u] - d4[e2 + u]);
+                        for (int u = 0; u < 2; ++u) {
+                            // LSE in log2 units, +inf for a row with no
+                            // visible key (weights exp2(x - inf) = 0, never inf)
+                            pv[u] = exp2_fast(fmaf(sacc[e + u], p.c2, -l4[e2 + u]));
+                            if constexpr (decltype(maskc)::value)
+                                pv[u] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, pv[u]) &
+                                                                      bit_mask(vis, acc_row(e + u)));
+                            dv2[u] = pv[u] * (dpacc[e + u] - d4[e2 + u]);
+                        }
+                        pp[e >> 3][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
+                        pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
                     }
-                    pp[e >> 3][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
-                    pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
                 }
-            }
+            };
+            if (block_unmasked(vis)) weights(mask_c<false>{});
+            else weights(mask_c<true>{});
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -503,18 +524,23 @@ void fa_bwd_dq_kernel(BwdParams p) {
             }
             const uint32_t vis = vis_bits(rel_lo - jt * T::R, rel_hi - jt * T::R);
             u32x4 pds[2];
+            auto weights = [&](auto maskc) __attribute__((always_inline)) {
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                float dv2[2];
+                for (int e = 0; e < 16; e += 2) {
+                    float dv2[2];
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const float x = exp2_fast(fmaf(sacc[e + u], p.c2, -lse2));
-                    const float pv = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, x) &
-                                                                   bit_mask(vis, acc_row(e + u)));
-                    dv2[u] = pv * (dpacc[e + u] - dd);
+                    for (int u = 0; u < 2; ++u) {
+                        float pv = exp2_fast(fmaf(sacc[e + u], p.c2, -lse2));
+                        if constexpr (decltype(maskc)::value)
+                            pv = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, pv) &
+                                                               bit_mask(vis, acc_row(e + u)));
+                        dv2[u] = pv * (dpacc[e + u] - dd);
+                    }
+                    pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
                 }
-                pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
-            }
+            };
+            if (block_unmasked(vis)) weights(mask_c<false>{});
+            else weights(mask_c<true>{});
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
