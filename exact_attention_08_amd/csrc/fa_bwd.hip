@@ -229,10 +229,10 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int NB = 4 * T::TB;                // blocks per stage
     constexpr int LPS = NB / T::NW + 2;          // copies per wave per stage
     static_assert(NB % T::NW == 0, "blocks split evenly over the waves");
-    auto issue = [&](int s) __attribute__((always_inline)) {
+    auto issue = [&](int s, int sq_i, int sh_i) __attribute__((always_inline)) {
         const bool valid = s < nsteps;
-        const int h = hkv * p.G + (valid ? s / nqb : 0);
-        const int i0 = (qb_a + (valid ? s % nqb : 0)) * T::R;
+        const int h = hkv * p.G + (valid ? sh_i : 0);
+        const int i0 = (qb_a + (valid ? sq_i : 0)) * T::R;
         const int rows = valid ? max(min(sq - i0, T::R), 0) : 0;
         const long long off = (((long long)b * sq + i0) * p.Hq + h) * D * 2;
         const i32x4 qrs = uniform_rsrc(make_rsrc((const char*)p.q + off, rows * tok_q));
@@ -264,11 +264,19 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) { dkt[db][e] = 0.f; dvt[db][e] = 0.f; }
 
     if (nsteps > 0) {
-        for (int s = 0; s < NS - 1; ++s) issue(s);
+        // query block and head of the next step to copy, and the query
+        // block of step s, advanced per step (no division in the loop)
+        int iq = 0, ih = 0, cq = 0;
+        for (int s = 0; s < NS - 1; ++s) {
+            issue(s, iq, ih);
+            if (++iq == nqb) { iq = 0; ++ih; }
+        }
         for (int s = 0; s < nsteps; ++s) {
             sync_step();
-            issue(s + NS - 1);
-            const int i0 = (qb_a + s % nqb) * T::R;
+            issue(s + NS - 1, iq, ih);
+            if (++iq == nqb) { iq = 0; ++ih; }
+            const int i0 = (qb_a + cq) * T::R;
+            if (++cq == nqb) cq = 0;
             // rows of this block that see a key of this wave: t = j - delta -
             // i spans [kw0 - delta - i0 - 31, kw0 + 31 - delta - i0]
             const int tmax = kw0 + T::R - 1 - delta - i0, tmin = kw0 - delta - i0 - (T::R - 1);
