@@ -229,18 +229,38 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     constexpr int NB = 4 * T::TB;                // blocks per stage
     constexpr int LPS = NB / T::NW + 2;          // copies per wave per stage
     static_assert(NB % T::NW == 0, "blocks split evenly over the waves");
-    auto issue = [&](int s, int sq_i, int sh_i) __attribute__((always_inline)) {
-        const bool valid = s < nsteps;
-        const int h = hkv * p.G + (valid ? sh_i : 0);
-        const int i0 = (qb_a + (valid ? sq_i : 0)) * T::R;
-        const int rows = valid ? max(min(sq - i0, T::R), 0) : 0;
-        const long long off = (((long long)b * sq + i0) * p.Hq + h) * D * 2;
-        const i32x4 qrs = uniform_rsrc(make_rsrc((const char*)p.q + off, rows * tok_q));
-        const i32x4 ors = uniform_rsrc(make_rsrc((const char*)p.dout + off, rows * tok_q));
+    // The copied step's first query row and head, the byte offset of its Q
+    // and dO rows and the element offset of its row terms; stepped by
+    // advance() (no multiplications in the loop but at a change of head).
+    struct Cursor {
+        int i0, h;
+        long long qo, ro;
+    };
+    auto cursor_at = [&](int ih) __attribute__((always_inline)) {
+        Cursor c;
+        c.i0 = qb_a * T::R;
+        c.h = hkv * p.G + ih;
+        c.qo = (((long long)b * sq + c.i0) * p.Hq + c.h) * D * 2;
+        c.ro = ((long long)b * p.Hq + c.h) * sq + c.i0;
+        return c;
+    };
+    auto advance = [&](Cursor& c, int& iq, int& ih) __attribute__((always_inline)) {
+        if (++iq == nqb) {
+            iq = 0;
+            c = cursor_at(++ih);
+        } else {
+            c.i0 += T::R;
+            c.qo += (long long)T::R * p.Hq * D * 2;
+            c.ro += T::R;
+        }
+    };
+    auto issue = [&](int s, const Cursor& cu) __attribute__((always_inline)) {
+        const int rows = s < nsteps ? max(min(sq - cu.i0, T::R), 0) : 0;
+        const i32x4 qrs = uniform_rsrc(make_rsrc((const char*)p.q + cu.qo, rows * tok_q));
+        const i32x4 ors = uniform_rsrc(make_rsrc((const char*)p.dout + cu.qo, rows * tok_q));
         const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + (s % NS) * SE));
-        const long long rb = ((long long)b * p.Hq + h) * sq + i0;
-        dma4_to_lds(uniform_rsrc(make_rsrc(p.lse2 + rb, rows * 4)), dst + 4 * TE * 2, lane * 4);
-        dma4_to_lds(uniform_rsrc(make_rsrc(p.dsum + rb, rows * 4)), dst + 4 * TE * 2 + 256, lane * 4);
+        dma4_to_lds(uniform_rsrc(make_rsrc(p.lse2 + cu.ro, rows * 4)), dst + 4 * TE * 2, lane * 4);
+        dma4_to_lds(uniform_rsrc(make_rsrc(p.dsum + cu.ro, rows * 4)), dst + 4 * TE * 2 + 256, lane * 4);
 #pragma unroll
         for (int c = 0; c < LPS - 2; ++c) {
             const int blk = wave + c * T::NW;    // 0 .. NB-1
@@ -267,14 +287,15 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
         // query block and head of the next step to copy, and the query
         // block of step s, advanced per step (no division in the loop)
         int iq = 0, ih = 0, cq = 0;
+        Cursor cur = cursor_at(0);
         for (int s = 0; s < NS - 1; ++s) {
-            issue(s, iq, ih);
-            if (++iq == nqb) { iq = 0; ++ih; }
+            issue(s, cur);
+            advance(cur, iq, ih);
         }
         for (int s = 0; s < nsteps; ++s) {
             sync_step();
-            issue(s + NS - 1, iq, ih);
-            if (++iq == nqb) { iq = 0; ++ih; }
+            issue(s + NS - 1, cur);
+            advance(cur, iq, ih);
             const int i0 = (qb_a + cq) * T::R;
             if (++cq == nqb) cq = 0;
             // rows of this block that see a key of this wave: t = j - delta -
