@@ -506,14 +506,14 @@ void fa_bwd_dq_kernel(BwdParams p) {
     static_assert(NB % T::NW == 0, "blocks split evenly over the waves");
     constexpr int LPS = NB / T::NW;
     const long long kvbase = ((long long)b * sk * p.Hkv + hkv) * D * 2;
-    auto issue = [&](int s) __attribute__((always_inline)) {
+    // copies of step s (tile tile_lo + s, K/V byte offset off) into ring
+    // slot si; past the last tile they read nothing (zero records)
+    auto issue = [&](int s, int si, long long off) __attribute__((always_inline)) {
         const int jt = tile_lo + s;
-        const bool valid = s < ntiles;
-        const int rows = valid ? max(min(sk - jt * T::R, T::R), 0) : 0;
-        const long long off = kvbase + (long long)(valid ? jt : 0) * T::R * tok_kv;
+        const int rows = s < ntiles ? max(min(sk - jt * T::R, T::R), 0) : 0;
         const i32x4 krs = uniform_rsrc(make_rsrc((const char*)p.k + off, rows * tok_kv));
         const i32x4 vrs = uniform_rsrc(make_rsrc((const char*)p.v + off, rows * tok_kv));
-        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + (s % NS) * 3 * TE));
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(ring + si * 3 * TE));
 #pragma unroll
         for (int c = 0; c < LPS; ++c) {
             const int blk = wave + c * T::NW;
@@ -533,12 +533,20 @@ void fa_bwd_dq_kernel(BwdParams p) {
         for (int e = 0; e < 16; ++e) dqt[db][e] = 0.f;
 
     if (ntiles > 0) {
-        for (int s = 0; s < NS - 1; ++s) issue(s);
+        // the copied step's K/V offset and the ring slots of the copied and
+        // the current step, advanced per step (no multiply or division)
+        const long long tile_step = (long long)T::R * tok_kv;
+        long long coff = kvbase + tile_lo * tile_step;
+        for (int s = 0; s < NS - 1; ++s, coff += tile_step) issue(s, s, coff);
+        int ci = NS - 1, si = 0;
         for (int s = 0; s < ntiles; ++s) {
             sync_step();
-            issue(s + NS - 1);
+            issue(s + NS - 1, ci, coff);
+            coff += tile_step;
+            ci = ci == NS - 1 ? 0 : ci + 1;
             const int jt = tile_lo + s;
-            const uint16_t* st = ring + (s % NS) * 3 * TE;
+            const uint16_t* st = ring + si * 3 * TE;
+            si = si == NS - 1 ? 0 : si + 1;
             const uint16_t* ka = st;
             const uint16_t* va = st + TE;
             const uint16_t* kt = st + 2 * TE;
