@@ -14,12 +14,13 @@
 //   fa_bwd_dkdv_kernel  one work-group per 256 keys of one K/V head: for
 //                       every query head of the group and every 32-row query
 //                       block that sees those keys
-//                           S = Q K^T,  P = exp2(S c2 - LSE_2),  dP = dO V^T,
+//                           S = Q K^T,  P = exp2(S c2 - LSE_2),
+//                           dP - D = dO V^T accumulated from -D,
 //                           dS = P (dP - D),  dV^T += dO^T P,  dK^T += Q^T dS;
 //   fa_bwd_dq_kernel    (enqueued first) one work-group per query block (the
 //                       query heads of one K/V head); first the row term of dS,
 //                       D_i = dO_i . O_i (O = the forward's output), which
-//                       it also stores for the next kernel; then for every
+//                       it also stores, negated, for the next kernel; then for every
 //                       32-key tile it sees
 //                           S^T = K Q^T,  dP^T = V dO^T,  the same P and dS,
 //                           dQ^T += K^T dS^T;
@@ -310,16 +311,24 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const float* lse_s = reinterpret_cast<const float*>(st + 4 * TE);
             const float* d_s = lse_s + 64;
 
-            // LSE (log2 units) and D of rows i0 + acc_row(e) + 4g
-            f32x16 sacc = {}, dpacc = {};
+            // dP starts from -D of its rows (element e: row i0 + acc_row(e) +
+            // 4g; the dQ kernel stores the row terms negated), so the
+            // accumulator ends as dP - D, the factor of dS
+            f32x16 sacc = {}, dpacc;
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 8 * q4 + 4 * g);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dpacc[4 * q4 + k] = d4[k];
+            }
 #pragma unroll
             for (int ks = 0; ks < T::KS; ++ks) {
                 sacc = mfma32x32x16<BF16>(a_operand<D>(qa, ks, lane), kop[ks], sacc);
                 dpacc = mfma32x32x16<BF16>(a_operand<D>(oa, ks, lane), vop[ks], dpacc);
             }
             // P and dS; element e is row i0 + acc_row(e) + 4g of key j.  The
-            // rows' LSE (log2 units) and D are read from the stage four at a
-            // time, where they are used.
+            // rows' LSE (log2 units) are read from the stage four at a time,
+            // where they are used.
             const int tb = j - delta - i0 - 4 * g;
             const int e_lo = tb - t_hi, e_hi = tb - t_lo;   // visible iff e_lo <= acc_row(e) <= e_hi
             const uint32_t vis = j < sk ? vis_bits(e_lo, e_hi) : 0u;
@@ -333,7 +342,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * q4 + 4 * g);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(d_s + 8 * q4 + 4 * g);
 #pragma unroll
                     for (int e2 = 0; e2 < 4; e2 += 2) {
                         const int e = 4 * q4 + e2;
@@ -346,7 +354,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                             if constexpr (decltype(maskc)::value)
                                 pv[u] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, pv[u]) &
                                                                       bit_mask(vis, acc_row(e + u)));
-                            dv2[u] = pv[u] * (dpacc[e + u] - d4[e2 + u]);
+                            dv2[u] = pv[u] * dpacc[e + u];
                         }
                         pp[e >> 3][(e & 7) >> 1] = pack2<BF16>(pv[0], pv[1]);
                         pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
@@ -487,7 +495,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
         dd = dd_row;
         if (g == 0) {                                     // for the dK/dV kernel, which runs next
-            p.dsum[ri] = dd;
+            p.dsum[ri] = -dd;
             p.lse2[ri] = lse2;
         }
     }
@@ -604,7 +612,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 
 template <int D, bool BF16>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
-    // dQ first: it also writes the row terms D the dK/dV kernel reads
+    // dQ first: it also writes the row terms -D the dK/dV kernel reads
     if (p.Sq > 0) {
         const long long n = (long long)p.nqb * (p.Hq / p.gw) * p.B;
         hipLaunchKernelGGL((fa_bwd_dq_kernel<D, BF16>), dim3((unsigned)n), dim3(64 * bwd_dq_waves(D)), 0, s, p);

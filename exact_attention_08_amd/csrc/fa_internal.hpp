@@ -99,7 +99,7 @@ struct BwdParams {
     void* dq;
     void* dk;
     void* dv;
-    float* dsum;                // workspace [B, Hq, Sq]: D_i = dO_i . O_i
+    float* dsum;                // workspace [B, Hq, Sq]: -D_i = -(dO_i . O_i)
     float* lse2;                // workspace [B, Hq, Sq]: LSE_i log2(e), +inf for empty rows
     int B, Hq, Hkv, G;
     int Sq, Sk;
