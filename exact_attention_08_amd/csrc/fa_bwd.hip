@@ -129,13 +129,6 @@ __device__ __forceinline__ u32x4 t_operand(const uint16_t* tile, int kk, int db,
 // Accumulator element e of a 32x32 MFMA result sits at row 8*(e/4) +
 // 4*(lane/32) + e%4 of the 32-row block: its offset without the lane term.
 __device__ __forceinline__ constexpr int acc_row(int e) { return 8 * (e >> 2) + (e & 3); }
-// The bits of a visibility word that acc_row(0..15) select.
-constexpr uint32_t kAccRowBits = 0x0f0f0f0fu;
-// true when every lane of the wave sees all 16 of its elements: the block
-// needs no mask (under a causal mask all blocks off the diagonal)
-__device__ __forceinline__ bool block_unmasked(uint32_t vis) {
-    return __builtin_amdgcn_ballot_w64((vis & kAccRowBits) != kAccRowBits) == 0ull;
-}
 template <bool B>
 struct mask_c {
     static constexpr bool value = B;
@@ -329,16 +322,20 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             // P and dS; element e is row i0 + acc_row(e) + 4g of key j.  The
             // rows' LSE (log2 units) are read from the stage four at a time,
             // where they are used.
-            const int tb = j - delta - i0 - 4 * g;
-            const int e_lo = tb - t_hi, e_hi = tb - t_lo;   // visible iff e_lo <= acc_row(e) <= e_hi
-            const uint32_t vis = j < sk ? vis_bits(e_lo, e_hi) : 0u;
             u32x4 pp[2], pds[2];
             auto weights = [&](auto maskc) __attribute__((always_inline)) {
                 // (distinct markers keep the compiler from hoisting the two
                 // versions' common arithmetic above the branch, which would
                 // hold all 32 intermediate values at once)
-                if constexpr (decltype(maskc)::value) asm volatile("; masked block");
-                else asm volatile("; unmasked block");
+                uint32_t vis = 0u;
+                if constexpr (decltype(maskc)::value) {
+                    asm volatile("; masked block");
+                    const int tb = j - delta - i0 - 4 * g;
+                    // visible iff tb - t_hi <= acc_row(e) <= tb - t_lo
+                    vis = j < sk ? vis_bits(tb - t_hi, tb - t_lo) : 0u;
+                } else {
+                    asm volatile("; unmasked block");
+                }
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 8 * q4 + 4 * g);
@@ -361,7 +358,9 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                     }
                 }
             };
-            if (block_unmasked(vis)) weights(mask_c<false>{});
+            // every (row, key) pair of the block visible (under a causal mask:
+            // all blocks off the diagonal): no mask
+            if (kw0 + T::R <= sk && tmin >= t_lo && tmax <= t_hi) weights(mask_c<false>{});
             else weights(mask_c<true>{});
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
@@ -567,9 +566,10 @@ void fa_bwd_dq_kernel(BwdParams p) {
                 sacc = mfma32x32x16<BF16>(a_operand<D>(ka, ks, lane), qop[ks], sacc);
                 dpacc = mfma32x32x16<BF16>(a_operand<D>(va, ks, lane), oop[ks], dpacc);
             }
-            const uint32_t vis = vis_bits(rel_lo - jt * T::R, rel_hi - jt * T::R);
             u32x4 pds[2];
             auto weights = [&](auto maskc) __attribute__((always_inline)) {
+                uint32_t vis = 0u;
+                if constexpr (decltype(maskc)::value) vis = vis_bits(rel_lo - jt * T::R, rel_hi - jt * T::R);
 #pragma unroll
                 for (int e = 0; e < 16; e += 2) {
                     float dv2[2];
@@ -584,7 +584,9 @@ void fa_bwd_dq_kernel(BwdParams p) {
                     pds[e >> 3][(e & 7) >> 1] = pack2<BF16>(dv2[0], dv2[1]);
                 }
             };
-            if (block_unmasked(vis)) weights(mask_c<false>{});
+            // every valid row of the wave sees every key of the tile (rows
+            // past the end have no weight anyway): no mask
+            if (lo_of(wlast) <= jt * T::R && hi_of(r0) >= jt * T::R + T::R - 1) weights(mask_c<false>{});
             else weights(mask_c<true>{});
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
