@@ -292,8 +292,17 @@ void fa_fwd_kernel(FwdParams p) {
         for (int ks = 0; ks < T::KS; ++ks) {
             const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
                 qrs, row * tok_bytes_q + (16 * ks + 8 * g) * 2, 0, 0);
-            qreg[ks] = x ^ p.qsign;                // exact negation when scale < 0
+            qreg[ks] = x;
         }
+        if (p.qsign) {                             // exact negation when scale < 0 (uniform)
+#pragma unroll
+            for (int ks = 0; ks < T::KS; ++ks) qreg[ks] ^= p.qsign;
+        }
+        // wait for the Q loads here, before any tile copy is issued (a wait
+        // the compiler placed at their first use, inside the loop, would
+        // drain the copies on every step)
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks) asm volatile("" ::"v"(qreg[ks]));
     }
 
     f32x16 oacc[T::DB];
