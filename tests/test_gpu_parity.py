@@ -96,6 +96,19 @@ VARLEN_CASES = [
     ("long_packed_d64", [100, 2100], [2300, 2100], 2, 2, 64, "fp16", False, (-1, -1), 206),
     ("wide_packed", [5400, 30, 0, 700], None, 4, 2, 128, "bf16", True, (-1, -1), 207),
     ("wide_packed_d64", [100, 2100], [2700, 2100], 2, 2, 64, "fp16", False, (-1, -1), 208),
+    # the longest-first order of up to 64 packed sequences: K/V heads that
+    # straddle XCDs (16) or share one (2), key lengths that differ from the
+    # query lengths, empty sequences, and more sequences than the order sorts
+    ("sorted_hkv16", [300, 0, 1000, 64, 65, 2], [40, 700, 1000, 64, 300, 2], 32, 16, 128, "bf16",
+     True, (-1, -1), 209),
+    ("sorted_hkv2", [33, 700, 5, 0, 128, 129, 900, 31, 64, 1, 250, 400], None, 8, 2, 128, "bf16",
+     True, (-1, -1), 210),
+    ("sorted_64_seqs", [(37 * i) % 260 for i in range(64)], None, 8, 1, 128, "bf16", True,
+     (-1, -1), 211),
+    ("unsorted_72_seqs", [(53 * i) % 190 for i in range(72)], None, 8, 1, 64, "fp16", True,
+     (-1, -1), 212),
+    ("sorted_wide", [5400, 30, 0, 7000, 2000, 6000, 1, 100], None, 4, 1, 128, "bf16", True,
+     (-1, -1), 213),
 ]
 
 
