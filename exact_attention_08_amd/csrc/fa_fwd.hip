@@ -32,11 +32,14 @@
 // Data movement.  K and V tiles of 32 keys go from HBM/L2 straight into LDS
 // with bounds-checked buffer loads (buffer_load_dwordx4 ... lds): rows past
 // the end of a sequence read as zeros, no staging registers, no branches.
-// Each lane of such a load picks its own 16-byte source chunk, so the tiles
-// are laid out in LDS in MFMA-operand order rather than row-major:
-//   * K: unit (ks, half, key) holds d-chunk 2*ks+half of that key, so the
-//     A operand of reduction step ks is one contiguous 1 KB wave read
-//     (ds_read_b128 at lane*16);
+// Each lane of such a load picks its own 16-byte source chunk, so a tile's
+// layout in LDS is free:
+//   * K at d = 128: row-major with the 16-byte chunks of key r XOR-swizzled
+//     by r % 16, so that each copy reads 4 whole rows and each A-operand read
+//     (lane = key, one chunk) touches every bank once; with ALiBi and at
+//     d = 64, operand order: unit (ks, half, key) holds d-chunk 2*ks+half of
+//     that key, so the A operand of reduction step ks is one contiguous 1 KB
+//     wave read (ds_read_b128 at lane*16);
 //   * V: 8-byte slot (kk, h, db, lane) holds the four columns that lane
 //     contributes to the gfx950 transpose read ds_read_b64_tr_b16 (16 lanes
 //     read a 4-key x 16-column block and each lane receives one column), so
@@ -104,6 +107,9 @@ void fa_fwd_kernel(FwdParams p) {
     using T = FwdGeo<D>;
     constexpr bool ALIBI = (MOD & 1) != 0, SOFTCAP = (MOD & 2) != 0;
     static_assert(!(VARLEN && MOD != 0), "score modifiers are padded-only");
+    // K tiles as whole rows (XOR-swizzled) rather than in operand order; not
+    // with ALiBi, whose extra registers would then spill
+    constexpr bool KROW = D == 128 && !ALIBI;
     constexpr int TE = T::TE;
     // K slots 0 .. STAGES-1, then V slots; after the key loop the first
     // 32 x D rows per wave stage the output
@@ -215,7 +221,13 @@ void fa_fwd_kernel(FwdParams p) {
     // ---- K/V ring in LDS, filled by DMA -----------------------------------
     // Tile pair s = (K_s, V_s): 2*TB 1 KB blocks; wave w issues blocks w,
     // w + NW, ...
-    //   K block kb = ks, lane L: key L%32, d-chunk 2*ks + L/32.
+    //   K block kb = ks, lane L: key L%32, d-chunk 2*ks + L/32 (operand
+    //   order), except with KROW (d = 128, no ALiBi): key 4*kb + L/16, the
+    //   key's 16-byte chunk (L%16) ^ (key%16), so that each copy reads 4
+    //   whole rows (32 bytes of 32 rows per copy measured 6 % slower on the
+    //   sliding window, 1-2 % on the causal and packed workloads) and chunk c
+    //   of key r sits at r*256 + 16*(c ^ (r%16)); the A-operand reads stay
+    //   conflict free (16 lanes = 16 keys, one chunk each, 16 distinct slots).
     //   V block vb, 16-byte unit u = 64*vb + L: half-block hb = u/32 =
     //   kh*DB + db, r = u%32 -> key 8*kh + 4*(r/16) + (r/2)%4, d-chunk
     //   4*db + 2*((r/8)%2) + r%2.
@@ -232,7 +244,12 @@ void fa_fwd_kernel(FwdParams p) {
         const int blk = dma_k[i] ? gb : gb - T::TB;
         dma_loff[i] = blk * 1024;
         if (dma_k[i]) {
-            dma_voff[i] = (lane & 31) * tok_bytes_kv + (2 * blk + (lane >> 5)) * 16;
+            if constexpr (KROW) {
+                const int row = 4 * blk + (lane >> 4);
+                dma_voff[i] = row * tok_bytes_kv + (((lane & 15) ^ (row & 15)) * 16);
+            } else {
+                dma_voff[i] = (lane & 31) * tok_bytes_kv + (2 * blk + (lane >> 5)) * 16;
+            }
         } else {
             const int hb = 2 * blk + (lane >> 5), r = lane & 31;
             const int kh = hb / T::DB, db = hb % T::DB;
@@ -424,7 +441,9 @@ void fa_fwd_kernel(FwdParams p) {
         const uint16_t* kt = kslot(i);
 #pragma unroll
         for (int ks = 0; ks < T::KS; ++ks)
-            kq[ks] = *reinterpret_cast<const u32x4*>(kt + ks * 512 + lane * 8);
+            kq[ks] = KROW
+                ? *reinterpret_cast<const u32x4*>(kt + (lane & 31) * D + (((2 * ks + (lane >> 5)) ^ (lane & 15)) * 8))
+                : *reinterpret_cast<const u32x4*>(kt + ks * 512 + lane * 8);
     };
     // operands of O^T += V^T P^T from the V tile in slot i; operand (kk, db)
     // holds keys 16kk + 8hh + 4g + 0..3 in half hh
