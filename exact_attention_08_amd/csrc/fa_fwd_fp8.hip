@@ -657,6 +657,12 @@ void fa_fwd_fp8_paired_kernel(Fp8Params p) {
     }
 
     // ---- copies HBM/L2 -> LDS ring (block layout of the kernel above) -----
+    // except K at d = 128 (KROW): row-major, each copy 8 whole 128-byte rows
+    // (lane L: key 8*blk + L/8, its 16-byte chunk (L%8) ^ ((key/2)%8)), so
+    // chunk c of key r sits at r*128 + 16*(c ^ ((r/2)%8)); the operand reads
+    // below (16 lanes = 16 keys, one chunk) then cover 16 distinct bank
+    // groups.  The operand-order copy read 32 bytes from each of 32 rows.
+    constexpr bool KROW = D == 128;
     const int tok_q = (int)p.q_tok_stride, tok_kv = (int)p.kv_tok_stride;
     const uint8_t* kseq = (const uint8_t*)p.k + ((long long)b * sk * p.Hkv + hkv) * D;
     const uint8_t* vtrow = (const uint8_t*)p.vt + ((long long)b * p.Hkv + hkv) * D * p.sk_pad;
@@ -668,7 +674,10 @@ void fa_fwd_fp8_paired_kernel(Fp8Params p) {
         const int blk = wave + i * T::NW;
         dma_isk[i] = blk < T::KBLK;
         dma_loff[i] = blk * 1024;
-        if (dma_isk[i]) {
+        if (dma_isk[i] && KROW) {
+            const int row = 8 * blk + (lane >> 3);
+            dma_voff[i] = row * tok_kv + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
+        } else if (dma_isk[i]) {
             const int hh = blk & 1, kc = (blk >> 1) % T::KC, st = (blk >> 1) / T::KC;
             dma_voff[i] = (32 * st + (lane & 31)) * tok_kv + 64 * kc + 32 * (lane >> 5) + 16 * hh;
         } else {
@@ -790,8 +799,21 @@ void fa_fwd_fp8_paired_kernel(Fp8Params p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) sacc[st][e] = 0.f;
 #pragma unroll
-                for (int kc = 0; kc < T::KC; ++kc)
-                    sacc[st] = mfma_f8(ld_op(tl + ((st * T::KC + kc) * 2) * 1024), qop[kc], sacc[st]);
+                for (int kc = 0; kc < T::KC; ++kc) {
+                    i32x8 a;
+                    if constexpr (KROW) {
+                        // key 32st + l%32, bytes 64kc + 32(l/32) .. +31 of it
+                        const uint8_t* kr = tl + (32 * st + (lane & 31)) * D;
+                        const int c = 4 * kc + 2 * (lane >> 5), sw = (lane >> 1) & 7;
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(kr + (c ^ sw) * 16);
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(kr + ((c + 1) ^ sw) * 16);
+                        a = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    } else {
+                        a = ld_op(tl + ((st * T::KC + kc) * 2) * 1024);
+                    }
+                    sacc[st] = mfma_f8(a, qop[kc], sacc[st]);
+                }
             }
             if (jt < in_lo || jt > in_hi) {
 #pragma unroll
